@@ -1,0 +1,21 @@
+"""CPU oracle of the fused MoE forward pass.
+
+TEST INFRASTRUCTURE: imported only by the tests, the smoke check and the
+benchmark's CPU-baseline leg. The HIP library never imports it.
+"""
+from .moe_oracle import (  # noqa: F401
+    combine_rows,
+    ep_mask_and_remap,
+    ep_partition,
+    forward,
+    grouped_down,
+    grouped_gate_up,
+    permute_indices,
+    permute_rows,
+    route,
+    silu,
+    slot_map,
+    softmax,
+    swiglu_mlp,
+    topk_ids,
+)
