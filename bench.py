@@ -1,0 +1,225 @@
+"""Benchmark of the fused MoE forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload NAME]
+                    [--no-cpu-baseline] [--copy-probe]
+
+One step is one moe_forward call (route, slot map, permute, grouped GEMM 1
+with SwiGLU, grouped GEMM 2, combine) over the whole synthetic batch, inputs
+and weights resident in HBM. The default workload is the redundant-slot
+layer (T=16384, H=4096, I=1024, 64 experts in 80 slots, top-8, Zipf(1.2)
+expert popularity), the largest of the layer shapes. Prints one JSON line.
+
+Timing: HIP events on the stream the kernels run on (torch's current
+stream), recorded by moe_forward itself at every stage boundary of every
+timed step; ms_per_step is the device time from the first to the last event.
+The dominant kernel (grouped GEMM 1) is timed by the events around it.
+
+--copy-probe runs only a plain device copy of a known size (for scaling the
+HBM byte counters of a profiler run) and exits.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused-MoE layer tokens/sec; grouped-GEMM TFLOP/s as % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_traffic.json")
+GEMM_SRC = os.path.join(ROOT, "moe_expert_dispatch_amd", "csrc", "gemm_bf16.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="redundant_slots_zipf")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe", action="store_true")
+    return ap.parse_args()
+
+
+def copy_probe():
+    import torch
+    n = 1 << 30  # 1 GiB read + 1 GiB written per copy
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+
+
+def gemm_traffic():
+    """HBM traffic of grouped GEMM 1 from the committed profiler summary, or
+    None if the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(GEMM_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if rec.get("kernel_source_sha256") != sha:
+            return None
+        return rec.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, seconds):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    cfg = inp.cfg
+    blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    block = 64
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        tok = np.arange(done, min(done + block, cfg.T))
+        oracle.forward(inp.x, inp.logits, inp.w_gate_up, inp.w_down, cfg.K, cfg.renormalize,
+                       cfg.ep_size, 0, tokens=tok)
+        done += tok.size
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= cfg.T:
+            break
+    return {"value": done / el, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": (f"first {done} of {cfg.T} tokens of the same workload through the fp64 "
+                       f"numpy oracle (route, EP mask / slot map, per-expert SwiGLU MLP, "
+                       f"combine), {el:.1f} s wall")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(expert-parallel shares run in sequence on one device); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import moe_expert_dispatch_amd as moe
+    from workloads import CONFIGS, build_slot_table, identity_slot_table, make_inputs, slot_weights
+
+    if args.copy_probe:
+        copy_probe()
+        return
+    moe.lib()
+    dev = torch.device("cuda:0")
+    cfg = CONFIGS[args.workload]
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    t_gen = time.perf_counter()
+    inp = make_inputs(cfg)
+    if cfg.n_replicated:
+        ro, rs, se = build_slot_table(cfg.E_local, inp.replicated_experts())
+        wgu_h, wd_h = inp.share_weights(0)
+        wgu = slot_weights(wgu_h, se).to(dev)
+        wd = slot_weights(wd_h, se).to(dev)
+        S = int(se.numel())
+    else:
+        ro, rs = identity_slot_table(cfg.E_local)
+        wgu_h, wd_h = inp.share_weights(0)
+        wgu, wd = wgu_h.contiguous().to(dev), wd_h.contiguous().to(dev)
+        S = cfg.E_local
+    x = inp.x.to(dev)
+    logits = inp.logits.to(dev)
+    ro, rs = ro.to(dev), rs.to(dev)
+    gen_s = time.perf_counter() - t_gen
+
+    fc = moe.ForwardConfig(T=cfg.T, H=cfg.H, I=cfg.I, E_global=cfg.E, K=cfg.K,
+                           renormalize=cfg.renormalize, S=S, dtype=tdt, ep_size=cfg.ep_size,
+                           ep_rank=0)
+    ws = torch.empty(moe.forward_workspace_size(fc), dtype=torch.uint8, device=dev)
+    out = torch.empty(cfg.T, cfg.H, dtype=tdt, device=dev)
+
+    # included pairs of this batch (all pairs when ep_size == 1)
+    ids, w = moe.route(logits, cfg.K, cfg.renormalize)
+    slot, wm, mask = moe.slot_map(ids, w, cfg.E, cfg.ep_size, 0, ro, rs)
+    P_in = int(mask.sum().item())
+
+    def step(events=None):
+        moe.forward(fc, x, wgu, wd, logits=logits, rep_off=ro, rep_slots=rs, out=out, ws=ws,
+                    events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # one set of stage events per timed step (created by a first record)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.NUM_EVENTS)]
+           for _ in range(args.steps)]
+    for row in ev:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step([e.cuda_event for e in ev[i]])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = ["route_slot_map", "permute", "gemm_gate_up", "gemm_down", "combine"]
+    stage_ms = {n: 0.0 for n in names}
+    for row in ev:
+        for j, n in enumerate(names):
+            stage_ms[n] += row[j].elapsed_time(row[j + 1]) / args.steps
+    ms_per_step = ev[0][0].elapsed_time(ev[-1][-1]) / args.steps
+
+    eb = 2 if cfg.dtype == "bf16" else 4
+    fl_gu = 4.0 * cfg.H * cfg.I * P_in       # gate and up products
+    fl_dn = 2.0 * cfg.H * cfg.I * P_in
+    gemm_tflops = (fl_gu + fl_dn) / ((stage_ms["gemm_gate_up"] + stage_ms["gemm_down"]) * 1e9)
+    gu_tflops = fl_gu / (stage_ms["gemm_gate_up"] * 1e9)
+    P = cfg.T * cfg.K
+    permute_bytes = cfg.T * cfg.H * eb + P_in * cfg.H * eb + 9 * P + 12 * P
+    combine_bytes = P_in * cfg.H * eb + 8 * P + cfg.T * cfg.H * eb
+    traffic = gemm_traffic()
+
+    res = {
+        "metric": METRIC,
+        "value": cfg.T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H,
+                   "intermediate": cfg.I, "experts": cfg.E, "slots": S, "top_k": cfg.K,
+                   "renormalize": cfg.renormalize, "ep_size": cfg.ep_size,
+                   "included_pairs": P_in, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_bf16 gate/up + SwiGLU",
+                     "achieved": gu_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gu_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
+        "grouped_gemm_tflops": gemm_tflops,
+        "grouped_gemm_frac_of_bf16_peak": gemm_tflops / PEAK_BF16_TFLOPS,
+        "stage_ms": stage_ms,
+        "permute_gbps": permute_bytes / (stage_ms["permute"] * 1e6),
+        "combine_gbps": combine_bytes / (stage_ms["combine"] * 1e6),
+        "host_wall_ms_per_step": wall * 1e3 / args.steps,
+        "input_generation_s": gen_s,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

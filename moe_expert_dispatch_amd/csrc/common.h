@@ -1,0 +1,102 @@
+// Internal helpers shared by the HIP kernels of the fused MoE forward pass
+// (gfx950, wave64). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16
+// bfloat16 is kept as raw uint16 bits: the top half of an IEEE binary32.
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round to nearest, ties to even; NaN stays NaN (quiet bit set).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------- wave ops
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return (l == 0) ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, off, kWave);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, kWave);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- misc
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline moe_status_t launch_status() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// Number of compute units of the current device (queried once per device).
+int device_cu_count();
+
+// ---------------------------------------------------------------- launchers
+// Host-side launchers; arguments are validated by the C-ABI layer.
+moe_status_t launch_route(const float* logits, int T, int E, int K, int renorm, int32_t* ids,
+                          float* w, hipStream_t stream);
+moe_status_t launch_slot_map(const int32_t* ids, const float* w, int T, int K, int start,
+                             int E_local, const int32_t* rep_off, const int32_t* rep_slots,
+                             int S, int32_t* slot, float* w_masked, uint8_t* mask,
+                             hipStream_t stream);
+
+struct PermutePlan {
+  int P;        // pairs
+  int chunk;    // pairs per chunk (multiple of 256)
+  int nchunks;  // ceil(P / chunk)
+  size_t ws_bytes;
+};
+PermutePlan permute_plan(int T, int K, int S);
+moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
+                            const int32_t* slot, const uint8_t* mask, int S, int32_t* offsets,
+                            int32_t* sorted_pairs, int32_t* pair_row, void* x_perm, void* ws,
+                            hipStream_t stream);
+
+moe_status_t launch_gemm_bf16(moe_gemm_op_t op, const void* a, const int32_t* offsets, int S,
+                              int max_rows, const void* w, int H, int I, void* c,
+                              hipStream_t stream);
+moe_status_t launch_gemm_f32(moe_gemm_op_t op, const void* a, const int32_t* offsets, int S,
+                             int max_rows, const void* w, int H, int I, void* c,
+                             hipStream_t stream);
+
+moe_status_t launch_combine(const void* y, moe_dtype_t y_dt, const int32_t* pair_row,
+                            const float* w_masked, int T, int K, int H, void* out,
+                            moe_dtype_t out_dt, int accumulate, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,313 @@
+// C ABI of the fused MoE forward pass: host-side argument validation,
+// workspace planning and the fused stage sequence. Every kernel launch is
+// asynchronous on the caller's stream; nothing here allocates or waits.
+//
+// Sources: TensorRT-LLM PR #10985 walkthrough (the fused op takes tokens,
+// selected experts and routing weights; MoE mapping configuration with EP
+// size / rank and max num tokens sizing the workspace); vLLM
+// ep_fused_moe_patch.py _ep_init (E % ep_size asserted, start = rank * E_l).
+#include <atomic>
+
+#include "common.h"
+
+namespace moe {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = 1;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool dtype_ok(moe_dtype_t dt) { return dt == MOE_DTYPE_F32 || dt == MOE_DTYPE_BF16; }
+int dtype_bytes(moe_dtype_t dt) { return dt == MOE_DTYPE_F32 ? 4 : 2; }
+
+// T * K and T * K * max(H, I) must stay addressable with 32-bit row indices.
+bool pairs_fit(int T, int K) { return (long long)T * K < (1LL << 31); }
+
+moe_status_t check_route(const float* logits, int T, int E, int K, const int32_t* ids,
+                         const float* w) {
+  if (T < 0 || E < 1 || K < 1 || K > E) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (!pairs_fit(T, K) || (long long)T * E >= (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && (!logits || !ids || !w)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status_t check_slot_map(const int32_t* ids, const float* w, int T, int K, int E_global,
+                            int ep_size, int ep_rank, const int32_t* rep_off,
+                            const int32_t* rep_slots, int S, const int32_t* slot,
+                            const float* w_masked, const uint8_t* mask) {
+  if (T < 0 || K < 1 || E_global < 1 || ep_size < 1) return MOE_ERR_INVALID_ARG;
+  if (E_global % ep_size != 0 || ep_rank < 0 || ep_rank >= ep_size) return MOE_ERR_INVALID_ARG;
+  const int E_local = E_global / ep_size;
+  if (S < E_local) return MOE_ERR_INVALID_ARG;
+  if (!rep_off && S != E_local) return MOE_ERR_INVALID_ARG;
+  if (rep_off && !rep_slots) return MOE_ERR_INVALID_ARG;
+  if (S > MOE_MAX_SLOTS || K > MOE_MAX_TOPK || E_global > MOE_MAX_EXPERTS)
+    return MOE_ERR_UNSUPPORTED;
+  if (!pairs_fit(T, K)) return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && (!ids || !w || !slot || !w_masked || !mask)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status_t check_permute(const void* x, moe_dtype_t dt, int T, int H, int K,
+                           const int32_t* slot, const uint8_t* mask, int S,
+                           const int32_t* offsets, const int32_t* sorted_pairs,
+                           const int32_t* pair_row, const void* x_perm, const void* ws,
+                           size_t ws_bytes) {
+  if (T < 0 || K < 1 || S < 1 || H < 1) return MOE_ERR_INVALID_ARG;
+  if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+  if (S > MOE_MAX_SLOTS || K > MOE_MAX_TOPK || H % 8 != 0 || !pairs_fit(T, K))
+    return MOE_ERR_UNSUPPORTED;
+  if (!offsets) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!slot || !mask || !sorted_pairs || !pair_row)) return MOE_ERR_INVALID_ARG;
+  if (x_perm && T > 0 && (!x || !aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
+  const size_t need = permute_plan(T, K, S).ws_bytes;
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+moe_status_t check_gemm(moe_gemm_op_t op, moe_dtype_t dt, const void* a, const int32_t* offsets,
+                        int S, int max_rows, const void* w, int H, int I, const void* c) {
+  if (op != MOE_GEMM_GATE_UP_SWIGLU && op != MOE_GEMM_DOWN) return MOE_ERR_INVALID_ARG;
+  if (S < 1 || max_rows < 0 || H < 1 || I < 1) return MOE_ERR_INVALID_ARG;
+  if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+  if (S > MOE_MAX_SLOTS || H % 8 != 0 || I % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((long long)max_rows * (H > I ? H : I) >= (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  if (!offsets) return MOE_ERR_INVALID_ARG;
+  if (max_rows > 0 && (!a || !w || !c)) return MOE_ERR_INVALID_ARG;
+  if (max_rows > 0 && (!aligned16(a) || !aligned16(w) || !aligned16(c)))
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status_t check_combine(const void* y, moe_dtype_t y_dt, const int32_t* pair_row,
+                           const float* w_masked, int T, int K, int H, const void* out,
+                           moe_dtype_t out_dt) {
+  if (T < 0 || K < 1 || H < 1) return MOE_ERR_INVALID_ARG;
+  if (!dtype_ok(y_dt) || !dtype_ok(out_dt)) return MOE_ERR_UNSUPPORTED;
+  if (K > MOE_MAX_TOPK || H % 8 != 0 || !pairs_fit(T, K)) return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && (!y || !pair_row || !w_masked || !out)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned16(y) || !aligned16(out))) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status_t launch_gemm(moe_gemm_op_t op, moe_dtype_t dt, const void* a, const int32_t* offsets,
+                         int S, int max_rows, const void* w, int H, int I, void* c,
+                         hipStream_t stream) {
+  return dt == MOE_DTYPE_BF16 ? launch_gemm_bf16(op, a, offsets, S, max_rows, w, H, I, c, stream)
+                              : launch_gemm_f32(op, a, offsets, S, max_rows, w, H, I, c, stream);
+}
+
+// Workspace of moe_forward, carved in this order (each 256-byte aligned).
+struct ForwardLayout {
+  size_t ids, w, slot, w_masked, mask, offsets, sorted_pairs, pair_row, perm_ws, x_perm, act;
+  size_t total;
+};
+
+ForwardLayout forward_layout(const moe_config_t* c) {
+  ForwardLayout L;
+  const size_t P = (size_t)c->T_max * c->K;
+  const size_t eb = dtype_bytes(c->dtype);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.ids = take(P * 4);
+  L.w = take(P * 4);
+  L.slot = take(P * 4);
+  L.w_masked = take(P * 4);
+  L.mask = take(P);
+  L.offsets = take(((size_t)c->S + 1) * 4);
+  L.sorted_pairs = take(P * 4);
+  L.pair_row = take(P * 4);
+  L.perm_ws = take(permute_plan(c->T_max, c->K, c->S).ws_bytes);
+  L.x_perm = take(P * c->H * eb);  // later reused for the down-projection output
+  L.act = take(P * c->I * eb);
+  L.total = off;
+  return L;
+}
+
+moe_status_t check_config(const moe_config_t* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->T_max < 0 || c->T < 0 || c->T > c->T_max) return MOE_ERR_INVALID_ARG;
+  if (c->H < 1 || c->I < 1 || c->E_global < 1 || c->K < 1 || c->K > c->E_global)
+    return MOE_ERR_INVALID_ARG;
+  if (c->ep_size < 1 || c->E_global % c->ep_size != 0 || c->ep_rank < 0 ||
+      c->ep_rank >= c->ep_size)
+    return MOE_ERR_INVALID_ARG;
+  if (c->S < c->E_global / c->ep_size) return MOE_ERR_INVALID_ARG;
+  if (!dtype_ok(c->dtype) || !dtype_ok(c->out_dtype)) return MOE_ERR_UNSUPPORTED;
+  if (c->E_global > MOE_MAX_EXPERTS || c->K > MOE_MAX_TOPK || c->S > MOE_MAX_SLOTS)
+    return MOE_ERR_UNSUPPORTED;
+  if (c->H % 8 != 0 || c->I % 8 != 0 || !pairs_fit(c->T_max, c->K)) return MOE_ERR_UNSUPPORTED;
+  const long long P = (long long)c->T_max * c->K;
+  if (P * (c->H > c->I ? c->H : c->I) >= (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_str(moe_status_t status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: dtype or shape not supported";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP launch or runtime error";
+  }
+  return "unknown moe_status_t";
+}
+
+moe_status_t moe_route(const float* logits, int T, int E, int K, int renormalize, int32_t* ids,
+                       float* w, hipStream_t stream) {
+  const moe_status_t st = check_route(logits, T, E, K, ids, w);
+  if (st != MOE_OK) return st;
+  return launch_route(logits, T, E, K, renormalize ? 1 : 0, ids, w, stream);
+}
+
+moe_status_t moe_slot_map(const int32_t* ids, const float* w, int T, int K, int E_global,
+                          int ep_size, int ep_rank, const int32_t* rep_off,
+                          const int32_t* rep_slots, int S, int32_t* slot, float* w_masked,
+                          uint8_t* mask, hipStream_t stream) {
+  const moe_status_t st = check_slot_map(ids, w, T, K, E_global, ep_size, ep_rank, rep_off,
+                                         rep_slots, S, slot, w_masked, mask);
+  if (st != MOE_OK) return st;
+  const int E_local = E_global / ep_size;
+  return launch_slot_map(ids, w, T, K, ep_rank * E_local, E_local, rep_off, rep_slots, S, slot,
+                         w_masked, mask, stream);
+}
+
+size_t moe_permute_workspace_size(int T, int K, int S) {
+  if (T < 0 || K < 1 || S < 1 || !pairs_fit(T, K)) return 0;
+  return permute_plan(T, K, S).ws_bytes;
+}
+
+moe_status_t moe_permute(const void* x, moe_dtype_t dt, int T, int H, int K,
+                         const int32_t* slot, const uint8_t* mask, int S, int32_t* offsets,
+                         int32_t* sorted_pairs, int32_t* pair_row, void* x_perm, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  const moe_status_t st = check_permute(x, dt, T, H, K, slot, mask, S, offsets, sorted_pairs,
+                                        pair_row, x_perm, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  return launch_permute(x, dtype_bytes(dt), T, H, K, slot, mask, S, offsets, sorted_pairs,
+                        pair_row, x_perm, ws, stream);
+}
+
+moe_status_t moe_grouped_gemm(moe_gemm_op_t op, moe_dtype_t dt, const void* a,
+                              const int32_t* offsets, int S, int max_rows, const void* w, int H,
+                              int I, void* c, hipStream_t stream) {
+  const moe_status_t st = check_gemm(op, dt, a, offsets, S, max_rows, w, H, I, c);
+  if (st != MOE_OK) return st;
+  return launch_gemm(op, dt, a, offsets, S, max_rows, w, H, I, c, stream);
+}
+
+moe_status_t moe_combine(const void* y, moe_dtype_t y_dt, const int32_t* pair_row,
+                         const float* w_masked, int T, int K, int H, void* out,
+                         moe_dtype_t out_dt, int accumulate, hipStream_t stream) {
+  const moe_status_t st = check_combine(y, y_dt, pair_row, w_masked, T, K, H, out, out_dt);
+  if (st != MOE_OK) return st;
+  return launch_combine(y, y_dt, pair_row, w_masked, T, K, H, out, out_dt, accumulate, stream);
+}
+
+size_t moe_forward_workspace_size(const moe_config_t* cfg) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  return forward_layout(cfg).total;
+}
+
+moe_status_t moe_forward(const moe_config_t* cfg, const moe_forward_args_t* args, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!args) return MOE_ERR_INVALID_ARG;
+  const int T = cfg->T, K = cfg->K, H = cfg->H, I = cfg->I, S = cfg->S;
+  const int E_local = cfg->E_global / cfg->ep_size;
+  if (!args->rep_off && S != E_local) return MOE_ERR_INVALID_ARG;
+  if (args->rep_off && !args->rep_slots) return MOE_ERR_INVALID_ARG;
+  if (T > 0) {
+    if (!args->x || !args->w_gate_up || !args->w_down || !args->out) return MOE_ERR_INVALID_ARG;
+    if (!args->logits && (!args->topk_ids || !args->topk_w)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(args->x) || !aligned16(args->w_gate_up) || !aligned16(args->w_down) ||
+        !aligned16(args->out))
+      return MOE_ERR_INVALID_ARG;
+  }
+  const ForwardLayout L = forward_layout(cfg);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_INVALID_ARG;
+
+  char* base = static_cast<char*>(ws);
+  int32_t* ids = reinterpret_cast<int32_t*>(base + L.ids);
+  float* w = reinterpret_cast<float*>(base + L.w);
+  int32_t* slot = reinterpret_cast<int32_t*>(base + L.slot);
+  float* w_masked = reinterpret_cast<float*>(base + L.w_masked);
+  uint8_t* mask = reinterpret_cast<uint8_t*>(base + L.mask);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  int32_t* sorted_pairs = reinterpret_cast<int32_t*>(base + L.sorted_pairs);
+  int32_t* pair_row = reinterpret_cast<int32_t*>(base + L.pair_row);
+  void* perm_ws = base + L.perm_ws;
+  void* x_perm = base + L.x_perm;
+  void* act = base + L.act;
+  void* y = x_perm;  // grouped GEMM 1 has consumed x_perm when GEMM 2 writes
+
+  auto mark = [&](int ev) -> moe_status_t {
+    if (args->events[ev] && hipEventRecord(args->events[ev], stream) != hipSuccess)
+      return MOE_ERR_HIP;
+    return MOE_OK;
+  };
+#define MOE_TRY(expr)                \
+  do {                               \
+    const moe_status_t s_ = (expr);  \
+    if (s_ != MOE_OK) return s_;     \
+  } while (0)
+
+  MOE_TRY(mark(MOE_EV_START));
+  const int32_t* ids_in = args->topk_ids;
+  const float* w_in = args->topk_w;
+  if (args->logits) {
+    MOE_TRY(launch_route(args->logits, T, cfg->E_global, K, cfg->renormalize ? 1 : 0, ids, w,
+                         stream));
+    ids_in = ids;
+    w_in = w;
+  }
+  MOE_TRY(launch_slot_map(ids_in, w_in, T, K, cfg->ep_rank * E_local, E_local, args->rep_off,
+                          args->rep_slots, S, slot, w_masked, mask, stream));
+  MOE_TRY(mark(MOE_EV_ROUTED));
+  MOE_TRY(launch_permute(args->x, dtype_bytes(cfg->dtype), T, H, K, slot, mask, S, offsets,
+                         sorted_pairs, pair_row, x_perm, perm_ws, stream));
+  MOE_TRY(mark(MOE_EV_PERMUTED));
+  MOE_TRY(launch_gemm(MOE_GEMM_GATE_UP_SWIGLU, cfg->dtype, x_perm, offsets, S, T * K,
+                      args->w_gate_up, H, I, act, stream));
+  MOE_TRY(mark(MOE_EV_GATE_UP));
+  MOE_TRY(launch_gemm(MOE_GEMM_DOWN, cfg->dtype, act, offsets, S, T * K, args->w_down, H, I, y,
+                      stream));
+  MOE_TRY(mark(MOE_EV_DOWN));
+  MOE_TRY(launch_combine(y, cfg->dtype, pair_row, w_masked, T, K, H, args->out, cfg->out_dtype,
+                         cfg->accumulate, stream));
+  MOE_TRY(mark(MOE_EV_COMBINED));
+#undef MOE_TRY
+  return MOE_OK;
+}
+
+}  // extern "C"

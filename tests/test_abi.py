@@ -1,0 +1,140 @@
+"""The C-ABI library loads and exports every declared entry point, and host
+validation rejects bad arguments before anything reaches a device.
+
+These tests make no compute call: every call here fails validation on the
+host (or only queries a workspace size), so no GPU is needed.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_expert_dispatch_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def so():
+    if not os.path.exists(moe.library_path()):
+        pytest.fail("libmoe_hip.so not built: run __graft_entry__.build()")
+    return moe.lib()
+
+
+def test_exports_every_declared_symbol(so):
+    names = declared_symbols()
+    assert set(names) == set(moe.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(so, n), n
+
+
+def test_status_strings(so):
+    for code in range(5):
+        assert moe.status_str(code).startswith("MOE_")
+
+
+def test_route_validation(so):
+    f = so.moe_route
+    assert f(None, 4, 4, 5, 1, None, None, None) == INVALID      # K > E
+    assert f(None, 4, 4, 0, 1, None, None, None) == INVALID      # K < 1
+    assert f(None, -1, 4, 2, 1, None, None, None) == INVALID     # T < 0
+    assert f(None, 4, 4, 2, 1, None, None, None) == INVALID      # null pointers
+    assert f(None, 4, 2048, 2, 1, None, None, None) == UNSUPPORTED  # E > 1024
+    assert f(None, 4, 64, 33, 1, None, None, None) == UNSUPPORTED   # K > 32
+
+
+def test_slot_map_validation(so):
+    f = so.moe_slot_map
+    # E_global % ep_size != 0 (the divisibility the EP partition asserts)
+    assert f(None, None, 1, 2, 10, 4, 0, None, None, 2, None, None, None, None) == INVALID
+    # ep_rank out of range
+    assert f(None, None, 1, 2, 8, 4, 4, None, None, 2, None, None, None, None) == INVALID
+    # S < E_local
+    assert f(None, None, 1, 2, 8, 2, 0, None, None, 3, None, None, None, None) == INVALID
+    # identity table needs S == E_local
+    assert f(None, None, 1, 2, 8, 2, 0, None, None, 5, None, None, None, None) == INVALID
+    # null data pointers
+    assert f(None, None, 1, 2, 8, 2, 0, None, None, 4, None, None, None, None) == INVALID
+
+
+def test_permute_validation_and_workspace(so):
+    ws = so.moe_permute_workspace_size
+    assert ws(0, 1, 1) > 0
+    assert ws(-1, 1, 1) == 0
+    # monotone in T for a fixed (K, S)
+    sizes = [ws(t, 8, 80) for t in range(0, 70000, 997)]
+    assert all(a <= b for a, b in zip(sizes, sizes[1:]))
+    f = so.moe_permute
+    assert f(None, 1, 4, 12, 2, None, None, 4, None, None, None, None, None, 0, None) == UNSUPPORTED  # H % 8
+    assert f(None, 1, 4, 16, 2, None, None, 4, None, None, None, None, None, 0, None) == INVALID
+    assert f(None, 7, 4, 16, 2, None, None, 4, None, None, None, None, None, 0, None) == UNSUPPORTED
+    fake = ctypes.c_void_p(256)
+    assert f(None, 1, 4, 16, 2, fake, fake, 4, fake, fake, fake, None, None, 0, None) == WORKSPACE
+
+
+def test_gemm_validation(so):
+    f = so.moe_grouped_gemm
+    fake = ctypes.c_void_p(256)
+    assert f(5, 1, fake, fake, 4, 16, fake, 64, 64, fake, None) == INVALID   # bad op
+    assert f(0, 1, fake, fake, 0, 16, fake, 64, 64, fake, None) == INVALID   # S < 1
+    assert f(0, 1, fake, fake, 4, 16, fake, 60, 64, fake, None) == UNSUPPORTED  # H % 8
+    assert f(0, 1, fake, fake, 4, 16, fake, 64, 68, fake, None) == UNSUPPORTED  # I % 8
+    assert f(0, 1, ctypes.c_void_p(264), fake, 4, 16, fake, 64, 64, fake, None) == INVALID  # misaligned
+    assert f(0, 1, None, fake, 4, 16, fake, 64, 64, fake, None) == INVALID   # null a
+
+
+def test_combine_validation(so):
+    f = so.moe_combine
+    fake = ctypes.c_void_p(256)
+    assert f(fake, 1, fake, fake, 4, 0, 64, fake, 1, 0, None) == INVALID     # K < 1
+    assert f(fake, 1, fake, fake, 4, 2, 60, fake, 1, 0, None) == UNSUPPORTED  # H % 8
+    assert f(None, 1, fake, fake, 4, 2, 64, fake, 1, 0, None) == INVALID
+    assert f(fake, 1, fake, fake, 4, 2, 64, ctypes.c_void_p(260), 1, 0, None) == INVALID
+
+
+def _cfg(**kw):
+    base = dict(T=16, H=64, I=64, E_global=8, K=2, renormalize=True, S=8,
+                dtype=__import__("torch").bfloat16)
+    base.update(kw)
+    return moe.ForwardConfig(**base)
+
+
+def test_forward_workspace_and_validation(so):
+    c = _cfg()
+    n = so.moe_forward_workspace_size(ctypes.byref(c.c_struct()))
+    P = 16 * 2
+    assert n >= P * (4 * 6 + 1) + P * 64 * 2 * 2  # index arrays + x_perm + activations
+    bad = [_cfg(K=9), _cfg(E_global=10, ep_size=4), _cfg(ep_size=2, ep_rank=2, S=4),
+           _cfg(S=3), _cfg(H=60), _cfg(T=32, T_max=16)]
+    for b in bad:
+        assert so.moe_forward_workspace_size(ctypes.byref(b.c_struct())) == 0
+    # workspace too small is reported before any launch
+    args = moe._ForwardArgs()
+    fake = 256
+    for name in ("x", "logits", "w_gate_up", "w_down", "out"):
+        setattr(args, name, fake)
+    st = so.moe_forward(ctypes.byref(c.c_struct()), ctypes.byref(args), ctypes.c_void_p(256),
+                        n - 1, None)
+    assert st == WORKSPACE
+    # identity table with S != E_local
+    c2 = _cfg(S=9)
+    n2 = so.moe_forward_workspace_size(ctypes.byref(c2.c_struct()))
+    st = so.moe_forward(ctypes.byref(c2.c_struct()), ctypes.byref(args), ctypes.c_void_p(256),
+                        n2, None)
+    assert st == INVALID
+
+
+def test_python_layer_rejects_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        moe.route(torch.zeros(4, 8), 2, True)
