@@ -13,43 +13,67 @@
 // `offsets`, so slots with no rows produce no items and no host readback of
 // the row counts is needed.
 //
-// Tiles: BM = 128 rows x 256 weight rows x BK = 64, 256 threads (4 waves in a
-// 2 x 2 layout). For the gate/up product the 256 weight rows are 128 gate
-// rows and the matching 128 up rows, so each block produces a 128 x 128 tile
-// of silu(G) * U without ever storing G or U. For the down product they are
-// 256 output columns. Both operands are K-contiguous in HBM and in LDS; LDS
-// rows are 128 bytes with the 16-byte chunks XOR-swizzled by (row mod 8) to
-// spread MFMA fragment reads over the banks. Two LDS stages: the next
-// K-slice is fetched into registers while the current one feeds the MFMAs.
+// Tiles: BM = 256 rows x 256 weight rows x BK = 64, 256 threads (4 waves in
+// a 2 x 2 layout, 128 x 128 per wave). For the gate/up product the 256
+// weight rows are 128 gate rows and the matching 128 up rows, so each block
+// produces a 256 x 128 tile of silu(G) * U without ever storing G or U. For
+// the down product they are 256 output columns. Both operands are
+// K-contiguous in HBM and in LDS; LDS rows are 128 bytes with the 16-byte
+// chunks XOR-swizzled by (row mod 8), which keeps the MFMA fragment reads
+// free of bank conflicts. Two LDS stages: the next K-slice is fetched into
+// registers while the current one feeds the MFMAs.
 //
-// MFMA: v_mfma_f32_16x16x32_bf16. A fragment: lane l holds 8 consecutive K
-// values of row (l mod 16); B fragment: 8 K values of weight row (l mod 16),
-// the same K block for both operands; the accumulator holds rows
-// 4*(l/16) + v, v = 0..3, of column (l mod 16).
+// MFMA: v_mfma_f32_32x32x16_bf16 with the weight fragment as the first
+// operand and the activation fragment as the second. Lane l supplies 8
+// consecutive K values (block l/32 of the 16) of weight row (l mod 32) and of
+// token row (l mod 32); the same K block for both operands, so the pairing
+// of K values is consistent. Accumulator register v of lane l then holds
+// output column 8*(v/4) + 4*(l/32) + (v mod 4) of token row (l mod 32): four
+// runs of 4 consecutive columns, stored as 8-byte words. Fragments are
+// double-buffered in registers so the LDS reads of the next K-16 step overlap
+// the MFMAs of the current one.
 //
 // Item order: with G blocks (one per CU), round r gives block b the item
 // r*G + (b mod 8)*(G/8) + b/8. Blocks b, b+8, ... run on the same XCD (the
 // dispatcher deals workgroups to the 8 XCDs round-robin), so each XCD works
-// on a contiguous run of items: the column tiles of a row tile, which share
-// the activation rows, and neighbouring row tiles of one slot, which share
-// the weight panel, meet in the same L2.
+// on a contiguous run of 32 items per round. Items are numbered in groups of
+// GM row tiles x GN column tiles (GN = min(column tiles, 8), GM = 32 / GN),
+// so one XCD's 32 concurrent items share GM activation tiles and GN weight
+// panels in its L2.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128;
+constexpr int BM = 256;
 constexpr int BK = 64;
 constexpr int BROWS = 256;  // weight rows per stage
 constexpr int NTHR = 256;
+constexpr int XCD_ITEMS = 32;  // concurrent items per XCD per round
 constexpr int A_VEC = BM * BK / 8;     // 16-byte vectors per A stage (1024)
 constexpr int B_VEC = BROWS * BK / 8;  // 2048
 constexpr int STAGE_VEC = A_VEC + B_VEC;
 
 __device__ __forceinline__ int swz(int row, int ch) { return row * 8 + (ch ^ (row & 7)); }
+
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOOB = 0x80000000u;  // beyond every resource size used here
+
+// Raw buffer resource over [base, base + bytes): stride 0, gfx9 data format word.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  const int32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
 
 // Builds tp[0..S] = prefix over slots of ceil(n_s / BM) in LDS.
 __device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int S, int32_t* tp,
@@ -87,6 +111,21 @@ __device__ __forceinline__ int find_slot(const int32_t* tp, int S, int rt) {
   return lo;
 }
 
+// Maps item w to (row tile, column tile) in GM x GN groups; false for the
+// holes of partial groups.
+__device__ __forceinline__ bool item_tile(int w, int RT, int CT, int GM, int GN, int* rt,
+                                          int* ct) {
+  const int per = GM * GN;
+  const int group = w / per;
+  const int within = w - group * per;
+  const int ncg = ceil_div(CT, GN);
+  const int rg = group / ncg;
+  const int cg = group - rg * ncg;
+  *rt = rg * GM + within / GN;
+  *ct = cg * GN + within % GN;
+  return *rt < RT && *ct < CT;
+}
+
 // OP 0: gate/up + SwiGLU (Kd = H, N = I, weight rows per slot 2I).
 // OP 1: down (Kd = I, N = H, weight rows per slot H).
 template <int OP>
@@ -100,24 +139,27 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  const int kvec = Kd / 8;                       // 16-byte vectors per row
+  const int wm = wave >> 1;  // 128-row half of the tile
+  const int wn = wave & 1;   // 128-weight-row half of the tile
+  const int kvec = Kd / 8;   // 16-byte vectors per row
   const size_t w_rows = (OP == 0) ? 2 * (size_t)N : (size_t)N;
-  const int BN = (OP == 0) ? 128 : 256;          // output columns per tile
+  const int BN = (OP == 0) ? BROWS / 2 : BROWS;  // output columns per tile
   const int CT = ceil_div(N, BN);
+  const int GN = CT < 8 ? CT : 8;
+  const int GM = XCD_ITEMS / GN;
   const int nk = ceil_div(Kd, BK);
 
   build_tile_prefix(offsets, S, tp, scan_scratch);
-  const int total = tp[S] * CT;
+  const int RT = tp[S];
+  const int total = ceil_div(RT, GM) * GM * ceil_div(CT, GN) * GN;
 
   const int G = gridDim.x;
   const int b = blockIdx.x;
-  const int slot_in_round = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+  const int first = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
 
-  for (int item = slot_in_round; item < total; item += G) {
-    const int rt = item / CT;
-    const int ct = item - rt * CT;
+  for (int item = first; item < total; item += G) {
+    int rt, ct;
+    if (!item_tile(item, RT, CT, GM, GN, &rt, &ct)) continue;  // block-uniform
     const int s = find_slot(tp, S, rt);
     const int row0 = offsets[s] + (rt - tp[s]) * BM;
     const int rows = min(BM, offsets[s + 1] - row0);
@@ -125,42 +167,41 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_kernel(
     const uint4* Ab = A + (size_t)row0 * kvec;
     const uint4* Wb = W + (size_t)s * w_rows * kvec;
 
-    // Per-thread global source rows for this item (fixed across K).
-    const uint4* a_src[A_VEC / NTHR];
-    bool a_ok[A_VEC / NTHR];
-#pragma unroll
-    for (int i = 0; i < A_VEC / NTHR; ++i) {
-      const int r = (i * NTHR + tid) >> 3;
-      a_ok[i] = r < rows;
-      a_src[i] = Ab + (size_t)r * kvec + (tid & 7);
-    }
-    const uint4* b_src[B_VEC / NTHR];
-    bool b_ok[B_VEC / NTHR];
+    // Global loads are raw buffer loads: every byte offset sits in the 32-bit
+    // per-lane offset, so the hardware range check (offset >= the resource's
+    // size reads as 0) zero-fills rows past the slot's end; K and column tails
+    // use an offset that is always out of range.
+    const __amdgpu_buffer_rsrc_t ra_rsrc =
+        make_rsrc(Ab, (uint32_t)rows * (uint32_t)Kd * 2u);
+    const __amdgpu_buffer_rsrc_t rb_rsrc =
+        make_rsrc(Wb, (uint32_t)w_rows * (uint32_t)Kd * 2u);
+    const uint32_t row_bytes = (uint32_t)Kd * 2u;
+    const uint32_t a_vo = (uint32_t)(tid >> 3) * row_bytes + (uint32_t)(tid & 7) * 16u;
+    uint32_t b_vo[B_VEC / NTHR];
 #pragma unroll
     for (int i = 0; i < B_VEC / NTHR; ++i) {
-      const int r = (i * NTHR + tid) >> 3;
+      const int r = i * (NTHR / 8) + (tid >> 3);
       int j, wrow;
       if (OP == 0) {
-        j = col0 + (r & 127);
-        wrow = (r >> 7) ? N + j : j;
+        j = col0 + (r & (BROWS / 2 - 1));
+        wrow = (r >= BROWS / 2) ? N + j : j;
       } else {
         j = col0 + r;
         wrow = j;
       }
-      b_ok[i] = j < N;
-      b_src[i] = Wb + (size_t)(b_ok[i] ? wrow : 0) * kvec + (tid & 7);
+      b_vo[i] = j < N ? (uint32_t)wrow * row_bytes + (uint32_t)(tid & 7) * 16u : kOOB;
     }
 
     uint4 ra[A_VEC / NTHR], rb[B_VEC / NTHR];
     auto load_stage = [&](int kt) {
-      const int kv = kt * (BK / 8);
-      const bool k_ok = kv + (tid & 7) < kvec;
+      const uint32_t kb = (uint32_t)kt * (BK * 2);
+      const bool k_ok = kt * (BK / 8) + (tid & 7) < kvec;
 #pragma unroll
       for (int i = 0; i < A_VEC / NTHR; ++i)
-        ra[i] = (a_ok[i] && k_ok) ? a_src[i][kv] : make_uint4(0, 0, 0, 0);
+        ra[i] = buf_load16(ra_rsrc, k_ok ? a_vo + (uint32_t)i * (NTHR / 8) * row_bytes + kb : kOOB);
 #pragma unroll
       for (int i = 0; i < B_VEC / NTHR; ++i)
-        rb[i] = (b_ok[i] && k_ok) ? b_src[i][kv] : make_uint4(0, 0, 0, 0);
+        rb[i] = buf_load16(rb_rsrc, (k_ok && b_vo[i] != kOOB) ? b_vo[i] + kb : kOOB);
     };
     auto store_stage = [&](int buf) {
       uint4* sa = smem + buf * STAGE_VEC;
@@ -177,76 +218,126 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_kernel(
       }
     };
 
-    floatx4 acc[4][8];
+    // acc[j][i]: weight-row subtile j (32 rows) x activation-row subtile i (32 rows).
+    floatx16 acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
 
-    __syncthreads();  // previous item's readers are done with both buffers
+    // LDS rows read by this lane: activation subtile i and weight subtile j.
+    int a_row[4], b_row[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a_row[i] = wm * 128 + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (OP == 0)  // j < 2: gate rows, j >= 2: the matching up rows
+        b_row[j] = (j < 2 ? 0 : BROWS / 2) + wn * 64 + (j & 1) * 32 + (lane & 31);
+      else
+        b_row[j] = wn * 128 + j * 32 + (lane & 31);
+    }
+
+    __syncthreads();  // the previous item's readers are done with both buffers
     load_stage(0);
     store_stage(0);
     __syncthreads();
 
-    for (int kt = 0; kt < nk; ++kt) {
+    // One K-step over LDS buffer `cur`; with HAS_NEXT it also fetches K-slice
+    // kt+1 from global memory and stores it into the other buffer. The
+    // scheduling groups at the end interleave, per K-16 sub-step, the 16 MFMAs
+    // with the LDS reads of the next sub-step's fragments, the global loads of
+    // the next stage (first sub-step) and its LDS stores (last sub-step).
+    auto kstep = [&](int kt, auto has_next) {
+      constexpr bool HAS_NEXT = decltype(has_next)::value;
       const int cur = kt & 1;
-      if (kt + 1 < nk) load_stage(kt + 1);
       const uint4* sa = smem + cur * STAGE_VEC;
       const uint4* sb = sa + A_VEC;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int ch = kk * 4 + (lane >> 4);
-        bf16x8_t fa[4], fb[8];
+      bf16x8_t fa[2][4], fb[2][4];
+      auto load_frags = [&](int kk, int buf) {
+        const int ch = kk * 2 + (lane >> 5);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = wm * 64 + i * 16 + (lane & 15);
-          const uint4 v = sa[swz(r, ch)];
-          fa[i] = *reinterpret_cast<const bf16x8_t*>(&v);
+          const uint4 v = sa[swz(a_row[i], ch)];
+          fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(&v);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          int r;
-          if (OP == 0)
-            r = (j < 4 ? 0 : 128) + wn * 64 + (j & 3) * 16 + (lane & 15);
-          else
-            r = wn * 128 + j * 16 + (lane & 15);
-          const uint4 v = sb[swz(r, ch)];
-          fb[j] = *reinterpret_cast<const bf16x8_t*>(&v);
+        for (int j = 0; j < 4; ++j) {
+          const uint4 v = sb[swz(b_row[j], ch)];
+          fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(&v);
         }
+      };
+      load_frags(0, 0);
+      if (HAS_NEXT) load_stage(kt + 1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        if (kk + 1 < BK / 16) load_frags(kk + 1, (kk + 1) & 1);
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i],
+                                                                acc[j][i], 0, 0, 0);
       }
-      if (kt + 1 < nk) store_stage(cur ^ 1);
+      if (HAS_NEXT) store_stage(cur ^ 1);
+      // Instruction groups: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read, 0x200 DS write.
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // fragments of sub-step 0
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {                         // sub-step 0
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (HAS_NEXT) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+      }
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {                        // sub-steps 1 and 2
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {                        // sub-step 3
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (HAS_NEXT) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
       __syncthreads();
-    }
+    };
+    for (int kt = 0; kt + 1 < nk; ++kt) kstep(kt, std::true_type{});
+    kstep(nk - 1, std::false_type{});
 
-    // Epilogue: f32 accumulators -> (SwiGLU) -> bf16, rounded once.
+    // Epilogue: f32 accumulators -> (SwiGLU) -> bf16, rounded once; each lane
+    // stores runs of 4 consecutive columns of one row as 8-byte words.
     uint16_t* Cb = C + (size_t)row0 * N;
+    const int cq = 4 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const int r = a_row[i];
+      if (r >= rows) continue;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = wm * 64 + i * 16 + 4 * (lane >> 4) + v;
-        if (r >= rows) continue;
+      for (int g = 0; g < 4; ++g) {  // run of 4 columns: accumulator registers 4g..4g+3
         if (OP == 0) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int col = col0 + wn * 64 + j * 16 + (lane & 15);
+          for (int j = 0; j < 2; ++j) {
+            const int col = col0 + wn * 64 + j * 32 + 8 * g + cq;
             if (col < N) {
-              const float g = acc[i][j][v];
-              const float u = acc[i][j + 4][v];
-              const float val = g / (1.0f + expf(-g)) * u;
-              Cb[(size_t)r * N + col] = (uint16_t)f32_to_bf16(val);
+              float o[4];
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const float gt = acc[j][i][4 * g + v];
+                const float up = acc[j + 2][i][4 * g + v];
+                o[v] = gt / (1.0f + expf(-gt)) * up;
+              }
+              *reinterpret_cast<uint2*>(Cb + (size_t)r * N + col) =
+                  make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
             }
           }
         } else {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int col = col0 + wn * 128 + j * 16 + (lane & 15);
-            if (col < N) Cb[(size_t)r * N + col] = (uint16_t)f32_to_bf16(acc[i][j][v]);
+          for (int j = 0; j < 4; ++j) {
+            const int col = col0 + wn * 128 + j * 32 + 8 * g + cq;
+            if (col < N)
+              *reinterpret_cast<uint2*>(Cb + (size_t)r * N + col) =
+                  make_uint2(pack_bf16x2(acc[j][i][4 * g], acc[j][i][4 * g + 1]),
+                             pack_bf16x2(acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]));
           }
         }
       }
@@ -262,10 +353,12 @@ moe_status_t launch_gemm_bf16(moe_gemm_op_t op, const void* a, const int32_t* of
   if (max_rows == 0) return MOE_OK;
   const int N = (op == MOE_GEMM_GATE_UP_SWIGLU) ? I : H;
   const int Kd = (op == MOE_GEMM_GATE_UP_SWIGLU) ? H : I;
-  const int BN = (op == MOE_GEMM_GATE_UP_SWIGLU) ? 128 : 256;
-  // Upper bound on items: sum_s ceil(n_s/BM) <= ceil(max_rows/BM) + min(S, max_rows).
+  const int BN = (op == MOE_GEMM_GATE_UP_SWIGLU) ? BROWS / 2 : BROWS;
+  // Upper bound on items: sum_s ceil(n_s/BM) <= ceil(max_rows/BM) + min(S, max_rows),
+  // plus the holes of partial item groups.
   const long long max_items =
-      (long long)(ceil_div(max_rows, BM) + (S < max_rows ? S : max_rows)) * ceil_div(N, BN);
+      (long long)(ceil_div(max_rows, BM) + (S < max_rows ? S : max_rows) + XCD_ITEMS) *
+      (ceil_div(N, BN) + 8);
   int G = device_cu_count();
   if (max_items < G) G = (int)max_items;
   if (op == MOE_GEMM_GATE_UP_SWIGLU)
