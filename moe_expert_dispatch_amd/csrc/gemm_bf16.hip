@@ -101,6 +101,10 @@ __device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int S, in
   __syncthreads();
 }
 
+// Block-uniform values read from LDS or memory are moved to scalar registers,
+// so buffer descriptors built from them are known to be uniform.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // Largest s in [0, S) with tp[s] <= rt (always a non-empty slot).
 __device__ __forceinline__ int find_slot(const int32_t* tp, int S, int rt) {
   int lo = 0, hi = S;  // invariant: tp[lo] <= rt < tp[hi]
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_kernel(
   const int nk = ceil_div(Kd, BK);
 
   build_tile_prefix(offsets, S, tp, scan_scratch);
-  const int RT = tp[S];
+  const int RT = uniform(tp[S]);
   const int total = ceil_div(RT, GM) * GM * ceil_div(CT, GN) * GN;
 
   const int G = gridDim.x;
@@ -160,9 +164,9 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_kernel(
   for (int item = first; item < total; item += G) {
     int rt, ct;
     if (!item_tile(item, RT, CT, GM, GN, &rt, &ct)) continue;  // block-uniform
-    const int s = find_slot(tp, S, rt);
-    const int row0 = offsets[s] + (rt - tp[s]) * BM;
-    const int rows = min(BM, offsets[s + 1] - row0);
+    const int s = uniform(find_slot(tp, S, rt));
+    const int row0 = uniform(offsets[s] + (rt - tp[s]) * BM);
+    const int rows = uniform(min(BM, offsets[s + 1] - row0));
     const int col0 = ct * BN;
     const uint4* Ab = A + (size_t)row0 * kvec;
     const uint4* Wb = W + (size_t)s * w_rows * kvec;

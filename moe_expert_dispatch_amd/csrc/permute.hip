@@ -12,9 +12,9 @@
 //   2. scan    one block: exclusive scan of hist in slot-major order, which
 //              yields each (slot, chunk) base row; offsets[s] = base of
 //              (s, chunk 0) and offsets[S] = P_in.
-//   3. scatter one wave per chunk walks its pairs in order, 64 at a time;
-//              lanes holding the same slot are ranked with a ballot, so the
-//              order inside a chunk is the pair order.
+//   3. scatter one block per chunk: batches of 64 pairs are ranked with a
+//              ballot per slot and per-batch counts are scanned in LDS, so
+//              the order inside a chunk is the pair order.
 //   4. gather  token-major: each token's row is read once and written to
 //              the K rows its included pairs occupy (16-byte vectors).
 #include "common.h"
@@ -29,6 +29,9 @@ __device__ __forceinline__ bool included(const int32_t* slot, const uint8_t* mas
   *s_out = s;
   return mask[p] != 0 && s >= 0 && s < S;
 }
+
+constexpr int kSub = 512;      // pairs per sub-chunk (8 batches of 64, 2 per wave)
+constexpr int kBatches = kSub / kWave;
 
 __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ slot,
                                                     const uint8_t* __restrict__ mask, int P,
@@ -49,72 +52,145 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
 }
 
 constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 8;                           // entries per thread per tile
+constexpr int kScanTile = kScanThreads * kScanPer;    // 8192 entries (32 KB of LDS)
 
+// Exclusive scan of hist[0..S*nchunks) in place, in tiles staged through LDS
+// (coalesced loads, all of a tile's loads in flight together).
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict__ hist, int S,
                                                             int nchunks,
                                                             int32_t* __restrict__ offsets) {
-  __shared__ int32_t partial[kScanThreads];
+  __shared__ int32_t tile[kScanTile];
+  __shared__ int32_t wsum[kScanThreads / kWave];
   const int N = S * nchunks;
   const int tid = threadIdx.x;
-  const int seg = ceil_div(N, kScanThreads);
-  const int lo = min(tid * seg, N);
-  const int hi = min(lo + seg, N);
-  int sum = 0;
-  for (int i = lo; i < hi; ++i) sum += hist[i];
-  partial[tid] = sum;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the per-thread sums.
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int v = tid >= off ? partial[tid - off] : 0;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  int carry = 0;
+  for (int base = 0; base < N; base += kScanTile) {
+    const int n = min(kScanTile, N - base);
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      const int i = k * kScanThreads + tid;
+      tile[i] = i < n ? hist[base + i] : 0;
+    }
     __syncthreads();
-    partial[tid] += v;
+    int v[kScanPer];
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      v[k] = tile[tid * kScanPer + k];
+      sum += v[k];
+    }
+    // inclusive scan of the per-thread sums: within the wave, then across waves
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int o = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += o;
+    }
+    if (lane == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+      int w = lane < kScanThreads / kWave ? wsum[lane] : 0;
+#pragma unroll
+      for (int off = 1; off < kScanThreads / kWave; off <<= 1) {
+        const int o = __shfl_up(w, off, kWave);
+        if (lane >= off) w += o;
+      }
+      if (lane < kScanThreads / kWave) wsum[lane] = w;
+    }
+    __syncthreads();
+    int run = carry + incl - sum + (wave > 0 ? wsum[wave - 1] : 0);
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      tile[tid * kScanPer + k] = run;
+      run += v[k];
+    }
+    const int tile_total = wsum[kScanThreads / kWave - 1];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      const int i = k * kScanThreads + tid;
+      if (i < n) hist[base + i] = tile[i];
+    }
+    carry += tile_total;
     __syncthreads();
   }
-  int run = partial[tid] - sum;  // exclusive prefix of this segment
-  for (int i = lo; i < hi; ++i) {
-    const int v = hist[i];
-    hist[i] = run;
-    run += v;
-  }
-  __syncthreads();
-  const int total = partial[kScanThreads - 1];
   for (int s = tid; s < S; s += kScanThreads)
     offsets[s] = nchunks > 0 ? hist[(size_t)s * nchunks] : 0;
-  if (tid == 0) offsets[S] = total;
+  if (tid == 0) offsets[S] = carry;
 }
 
-__global__ __launch_bounds__(kWave) void scatter_kernel(const int32_t* __restrict__ slot,
-                                                        const uint8_t* __restrict__ mask, int P,
-                                                        int S, int chunk, int nchunks,
-                                                        const int32_t* __restrict__ base,
-                                                        int32_t* __restrict__ sorted_pairs,
-                                                        int32_t* __restrict__ pair_row) {
-  extern __shared__ int32_t counter[];
+// One block (4 waves) per chunk. The chunk is walked in sub-chunks of 512
+// pairs = 8 batches of 64; wave w ranks batches 2w and 2w+1. Inside a batch the
+// lanes holding the same slot are ranked with a ballot (lane order = pair
+// order); per-batch slot counts, scanned over the batches, give each batch's
+// base row, so the order inside a slot is the pair order.
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ slot,
+                                                      const uint8_t* __restrict__ mask, int P,
+                                                      int S, int chunk, int nchunks,
+                                                      const int32_t* __restrict__ base,
+                                                      int32_t* __restrict__ sorted_pairs,
+                                                      int32_t* __restrict__ pair_row) {
+  extern __shared__ int32_t lds[];
+  int32_t* running = lds;       // [S] next free row per slot
+  int32_t* bcount = lds + S;    // [kBatches][S] counts, then base rows
   const int c = blockIdx.x;
+  const int tid = threadIdx.x;
   const int lane = lane_id();
-  for (int i = lane; i < S; i += kWave) counter[i] = base[(size_t)i * nchunks + c];
-  __syncthreads();
+  const int wave = tid / kWave;
+  for (int i = tid; i < S; i += blockDim.x) running[i] = base[(size_t)i * nchunks + c];
   const int p0 = c * chunk;
   const int p1 = min(p0 + chunk, P);
-  for (int pb = p0; pb < p1; pb += kWave) {
-    const int p = pb + lane;
-    int s = -1;
-    const bool inc = (p < p1) && included(slot, mask, p, P, S, &s);
-    int row = -1;
-    uint64_t active = __ballot(inc);
-    while (active) {
-      const int leader = __ffsll((unsigned long long)active) - 1;
-      const int ls = __shfl(s, leader, kWave);
-      const uint64_t same = __ballot(inc && s == ls);
-      const int b = counter[ls];
-      if (inc && s == ls) row = b + __popcll(same & lanemask_lt());
-      if (lane == leader) counter[ls] = b + __popcll(same);
-      active &= ~same;
+  for (int q0 = p0; q0 < p1; q0 += kSub) {
+    for (int i = tid; i < kBatches * S; i += blockDim.x) bcount[i] = 0;
+    __syncthreads();
+    constexpr int kPer = kBatches / 4;  // batches per wave
+    int s[kPer], rank[kPer];
+    bool inc[kPer];
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      const int p = q0 + (wave * kPer + m) * kWave + lane;
+      s[m] = -1;
+      inc[m] = p < p1 && included(slot, mask, p, P, S, &s[m]);
     }
-    if (p < p1) {
-      pair_row[p] = row;
-      if (row >= 0) sorted_pairs[row] = p;
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      const int b = wave * kPer + m;
+      rank[m] = 0;
+      uint64_t active = __ballot(inc[m]);
+      while (active) {
+        const int leader = __ffsll((unsigned long long)active) - 1;
+        const int ls = __shfl(s[m], leader, kWave);
+        const uint64_t same = __ballot(inc[m] && s[m] == ls);
+        if (inc[m] && s[m] == ls) rank[m] = __popcll(same & lanemask_lt());
+        if (lane == leader) bcount[b * S + ls] = __popcll(same);
+        active &= ~same;
+      }
     }
+    __syncthreads();
+    for (int i = tid; i < S; i += blockDim.x) {
+      int run = running[i];
+      for (int b = 0; b < kBatches; ++b) {
+        const int t = bcount[b * S + i];
+        bcount[b * S + i] = run;
+        run += t;
+      }
+      running[i] = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      const int b = wave * kPer + m;
+      const int p = q0 + b * kWave + lane;
+      if (p < p1) {
+        const int row = inc[m] ? bcount[b * S + s[m]] + rank[m] : -1;
+        pair_row[p] = row;
+        if (row >= 0) sorted_pairs[row] = p;
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -141,10 +217,12 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x
 PermutePlan permute_plan(int T, int K, int S) {
   PermutePlan pl;
   pl.P = T * K;
+  // At most max(1, 65536 / S) chunks, so the scan stays small; chunks are
+  // whole sub-chunks of 512 pairs.
   const int cap = S > 0 ? (65536 / S > 0 ? 65536 / S : 1) : 1;
-  const int units = ceil_div(pl.P, 256);
+  const int units = ceil_div(pl.P, kSub);
   const int n = units < cap ? units : cap;
-  pl.chunk = 256 * (n > 0 ? ceil_div(units, n) : 1);
+  pl.chunk = kSub * (n > 0 ? ceil_div(units, n) : 1);
   pl.nchunks = pl.P > 0 ? ceil_div(pl.P, pl.chunk) : 0;
   const int bound = n > 0 ? n : 1;  // min(units, cap), monotone in P
   pl.ws_bytes = (size_t)S * (size_t)bound * sizeof(int32_t);
@@ -164,8 +242,10 @@ moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
   }
   scan_kernel<<<1, kScanThreads, 0, stream>>>(hist, S, pl.nchunks, offsets);
   if (pl.nchunks > 0) {
-    scatter_kernel<<<pl.nchunks, kWave, lds, stream>>>(slot, mask, pl.P, S, pl.chunk,
-                                                      pl.nchunks, hist, sorted_pairs, pair_row);
+    const size_t lds_scatter = (size_t)(1 + kBatches) * S * sizeof(int32_t);
+    scatter_kernel<<<pl.nchunks, 256, lds_scatter, stream>>>(slot, mask, pl.P, S, pl.chunk,
+                                                            pl.nchunks, hist, sorted_pairs,
+                                                            pair_row);
   }
   if (x_perm != nullptr && T > 0) {
     const int nvec = H * elem_bytes / 16;
