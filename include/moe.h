@@ -89,9 +89,9 @@ const char* moe_status_str(moe_status_t status);
 
 /*
  * moe_route -- router softmax and top-K selection.
- *   Source: [EPMASK] docstring "topk routing produces global expert ids on
- *   ALL ranks (identical)" and the FusedMoE constructor's top_k /
- *   renormalize (default True) arguments.
+ *   Source: [EPMASK] module docstring, section "EP expert dispatch" (every
+ *   rank computes the same global top-k expert ids) and the FusedMoE
+ *   constructor's top_k / renormalize (default True) arguments.
  *
  * logits [T, E] f32 (input). For each token t:
  *   m = max_e logits[t, e];  p_e = exp(logits[t,e] - m) / sum_j exp(logits[t,j] - m)
@@ -179,8 +179,8 @@ moe_status_t moe_permute(const void* x, moe_dtype_t dt, int T, int H, int K,
  * Accumulation is f32; c is rounded once to dt. max_rows is the row
  * capacity of a and c (T*K from moe_permute); offsets[S] <= max_rows is a
  * device-data precondition (rows beyond max_rows are never touched).
- * dt MOE_DTYPE_BF16 uses the MFMA path and needs H % 8 == 0, I % 8 == 0;
- * MOE_DTYPE_F32 uses a vector-FMA path and needs H % 4 == 0, I % 4 == 0.
+ * H % 8 == 0 and I % 8 == 0. dt MOE_DTYPE_BF16 runs on the matrix cores
+ * (MFMA); MOE_DTYPE_F32 uses a vector fused-multiply-add path.
  */
 moe_status_t moe_grouped_gemm(moe_gemm_op_t op, moe_dtype_t dt, const void* a,
                               const int32_t* offsets, int S, int max_rows, const void* w,

@@ -83,8 +83,8 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(_LIB_FILE):
             raise RuntimeError(
-                f"{_LIB_FILE} is missing: build it with `python -m moe_expert_dispatch_amd.build` "
-                "(or __graft_entry__.build()); there is no non-HIP fallback")
+                f"{_LIB_FILE} is missing: build it with `python -m moe_expert_dispatch_amd.build`; "
+                "there is no non-HIP fallback")
         so = ctypes.CDLL(_LIB_FILE)
         for name, (res, args) in _SIGS.items():
             fn = getattr(so, name)
