@@ -55,6 +55,7 @@ constexpr int BK = 64;
 constexpr int BROWS = 256;  // weight rows per stage
 constexpr int NTHR = 256;
 constexpr int XCD_ITEMS = 32;  // concurrent items per XCD per round
+constexpr int DMA_PER_STAGE = 8;  // direct-to-LDS instructions per wave per K-slice
 constexpr int A_VEC = BM * BK / 8;     // 16-byte vectors per A stage (1024)
 constexpr int B_VEC = BROWS * BK / 8;  // 2048
 constexpr int STAGE_VEC = A_VEC + B_VEC;
@@ -62,6 +63,7 @@ constexpr int STAGE_VEC = A_VEC + B_VEC;
 __device__ __forceinline__ int swz(int row, int ch) { return row * 8 + (ch ^ (row & 7)); }
 
 typedef int int32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr uint32_t kOOB = 0x80000000u;  // beyond every resource size used here
 
 // Raw buffer resource over [base, base + bytes): stride 0, gfx9 data format word.
@@ -349,6 +351,313 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant, used when K % 32 == 0. Same tiles, item order and
+// epilogue, with BK = 32 and four LDS stages of 32 KB filled by
+// buffer_load_dwordx4 ... lds: no registers hold prefetched data, so three
+// K-slices (96 KB per CU) are in flight while one is computed on.
+//
+// LDS rows are 64 bytes; the 16-byte chunk c of row r sits at c ^ ((r>>2)&3),
+// which keeps the 32-row fragment reads conflict-free. One DMA instruction
+// fills 1 KB of LDS linearly (lane L writes bytes 16L..16L+15), i.e. 16 rows x
+// 4 chunks, so lane L fetches the global chunk that belongs at that position.
+//
+// The fragment reads are issued as inline ds_read_b128 with explicit
+// lgkmcnt waits, and the DMA completion with explicit vmcnt waits: the
+// compiler's own tracking of LDS DMA would otherwise drain every pending
+// slice before each LDS read. Per K-step kt (buffer kt&3):
+//   half 0: MFMAs on K-16 block 0 (fragments in registers), each pair
+//           followed by one LDS read of block 1;
+//   wait:   block-1 reads complete; this wave's DMA of slice kt+1 complete
+//           (vmcnt <= 8: only slice kt+2 may be pending); workgroup barrier,
+//           after which slice kt+1 is complete for every wave and buffer
+//           (kt-1)&3 is no longer read by anyone;
+//   half 1: MFMAs on block 1, each pair with one DMA instruction of slice
+//           kt+3 (into buffer (kt+3)&3 = (kt-1)&3) and one LDS read of
+//           block 0 of slice kt+1.
+// Every step issues the same 8 DMA instructions per wave (slices past the
+// end use an out-of-range offset and move nothing), so the vmcnt accounting
+// is constant. The epilogue uses buffer stores with a fixed instruction
+// count; the next item's first three slices are issued before or after them
+// so that the wait for slice 0 stays within the 6-bit vmcnt.
+constexpr int DBK = 32;
+constexpr int DA_VEC = BM * DBK / 8;                 // 1024 vectors: A part of a stage
+constexpr int DSTAGE_VEC = (BM + BROWS) * DBK / 8;   // 2048 vectors = 32 KB
+constexpr int DSTAGE_BYTES = DSTAGE_VEC * 16;
+constexpr int DNSTAGE = 4;
+
+__device__ __forceinline__ int swz4(int row, int ch) { return row * 4 + (ch ^ ((row >> 2) & 3)); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+template <int OFF>
+__device__ __forceinline__ void lds_read16(bf16x8_t& d, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF));
+}
+
+// Waits for all LDS reads and ties the fragments to the wait, so no MFMA
+// using them is scheduled above it.
+__device__ __forceinline__ void lgkm_wait_frags(bf16x8_t (&fa)[4], bf16x8_t (&fb)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]), "+v"(fb[1]),
+                 "+v"(fb[2]), "+v"(fb[3]));
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
+}
+
+// Byte offset of weight fragment j from the lane's first weight row.
+template <int OP>
+constexpr int bfrag_off(int j) {
+  return (OP == 0 ? ((j < 2 ? 0 : BROWS / 2) + (j & 1) * 32) : j * 32) * 64;
+}
+
+template <int OP>
+__device__ __forceinline__ void read_frag(int x, bf16x8_t* fa, bf16x8_t* fb, uint32_t aa,
+                                          uint32_t ba) {
+  switch (x) {
+    case 0: lds_read16<0 * 2048>(fa[0], aa); break;
+    case 1: lds_read16<1 * 2048>(fa[1], aa); break;
+    case 2: lds_read16<2 * 2048>(fa[2], aa); break;
+    case 3: lds_read16<3 * 2048>(fa[3], aa); break;
+    case 4: lds_read16<bfrag_off<OP>(0)>(fb[0], ba); break;
+    case 5: lds_read16<bfrag_off<OP>(1)>(fb[1], ba); break;
+    case 6: lds_read16<bfrag_off<OP>(2)>(fb[2], ba); break;
+    default: lds_read16<bfrag_off<OP>(3)>(fb[3], ba); break;
+  }
+}
+
+typedef int int32x2_t __attribute__((ext_vector_type(2)));
+
+// One item of the direct-to-LDS kernel: tile geometry, buffer descriptors of
+// the activation rows, the weight panel and the output rows, and this lane's
+// DMA source offsets.
+struct DmaItem {
+  int rows, row0, col0;
+  __amdgpu_buffer_rsrc_t ra, rb, rc;
+  uint32_t a_off[4], b_off[4];
+};
+
+template <int OP>
+__global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_dma_kernel(
+    const uint4* __restrict__ A, const int32_t* __restrict__ offsets, int S,
+    const uint4* __restrict__ W, int N, int Kd, uint16_t* __restrict__ C) {
+  __shared__ uint4 smem[DNSTAGE * DSTAGE_VEC];
+  __shared__ int32_t tp[MOE_MAX_SLOTS + 1];
+  __shared__ int32_t scan_scratch[NTHR];
+
+  constexpr int kStores = OP == 0 ? 32 : 64;  // epilogue store instructions per wave
+  constexpr bool kDmaFirst = 2 * DMA_PER_STAGE + kStores <= 63;
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const size_t w_rows = (OP == 0) ? 2 * (size_t)N : (size_t)N;
+  const int BN = (OP == 0) ? BROWS / 2 : BROWS;
+  const int CT = ceil_div(N, BN);
+  const int GN = CT < 8 ? CT : 8;
+  const int GM = XCD_ITEMS / GN;
+  const int nk = Kd / DBK;
+  const uint32_t row_bytes = (uint32_t)Kd * 2u;
+
+  build_tile_prefix(offsets, S, tp, scan_scratch);
+  const int RT = uniform(tp[S]);
+  const int total = ceil_div(RT, GM) * GM * ceil_div(CT, GN) * GN;
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+
+  // Fragment rows of one operand differ by multiples of 32 rows (whole swizzle
+  // periods), so every fragment address is a per-lane base for the operand
+  // and K-half plus a compile-time offset.
+  const int a_row0 = wm * 128 + (lane & 31);
+  const int b_row0 = (OP == 0 ? wn * 64 : wn * 128) + (lane & 31);
+  const uint32_t a_lane0 = (uint32_t)swz4(a_row0, lane >> 5) * 16u;
+  const uint32_t a_lane1 = (uint32_t)swz4(a_row0, 2 + (lane >> 5)) * 16u;
+  const uint32_t b_lane0 = DA_VEC * 16u + (uint32_t)swz4(b_row0, lane >> 5) * 16u;
+  const uint32_t b_lane1 = DA_VEC * 16u + (uint32_t)swz4(b_row0, 2 + (lane >> 5)) * 16u;
+  const uint32_t smem_base = lds_addr(smem);
+
+  // Next valid item at or after w (block-uniform), or `total`.
+  auto next_item = [&](int w, int* rt, int* ct) {
+    while (w < total && !item_tile(w, RT, CT, GM, GN, rt, ct)) w += G;
+    return w;
+  };
+
+  auto setup = [&](int rt, int ct, DmaItem& x) {
+    const int s = uniform(find_slot(tp, S, rt));
+    x.row0 = uniform(offsets[s] + (rt - tp[s]) * BM);
+    x.rows = uniform(min(BM, offsets[s + 1] - x.row0));
+    x.col0 = ct * BN;
+    x.ra = make_rsrc(A + (size_t)x.row0 * (Kd / 8), (uint32_t)x.rows * row_bytes);
+    x.rb = make_rsrc(W + (size_t)s * w_rows * (Kd / 8), (uint32_t)w_rows * row_bytes);
+    x.rc = make_rsrc(C + (size_t)x.row0 * N, (uint32_t)x.rows * (uint32_t)N * 2u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = wave * 4 + i;  // 16-row block of the stage
+      const int r = q * 16 + (lane >> 2);
+      const int ch = (lane & 3) ^ ((r >> 2) & 3);
+      x.a_off[i] = (uint32_t)r * row_bytes + (uint32_t)ch * 16u;
+      int j, wrow;
+      if (OP == 0) {
+        j = x.col0 + (r & (BROWS / 2 - 1));
+        wrow = (r >= BROWS / 2) ? N + j : j;
+      } else {
+        j = x.col0 + r;
+        wrow = j;
+      }
+      x.b_off[i] = j < N ? (uint32_t)wrow * row_bytes + (uint32_t)ch * 16u : kOOB;
+    }
+  };
+  // DMA instruction q (0..7) of slice kt into its LDS stage buffer.
+  auto dma = [&](const DmaItem& x, int q, int kt) {
+    const int buf = kt & (DNSTAGE - 1);
+    const bool live = kt < nk;
+    const uint32_t kb = (uint32_t)kt * (DBK * 2);
+    uint4* stage = smem + buf * DSTAGE_VEC;
+    if (q < 4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          x.ra, (lds_ptr_t)(stage + (wave * 4 + q) * 64), 16, live ? x.a_off[q] + kb : kOOB, 0,
+          0, 0);
+    } else {
+      const int i = q - 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          x.rb, (lds_ptr_t)(stage + DA_VEC + (wave * 4 + i) * 64), 16,
+          (live && x.b_off[i] != kOOB) ? x.b_off[i] + kb : kOOB, 0, 0, 0);
+    }
+  };
+  auto issue_prologue = [&](const DmaItem& x) {
+#pragma unroll
+    for (int kt = 0; kt < 3; ++kt)
+#pragma unroll
+      for (int q = 0; q < DMA_PER_STAGE; ++q) dma(x, q, kt);
+  };
+
+  floatx16 acc[4][4];
+  bf16x8_t f0a[4], f0b[4], f1a[4], f1b[4];
+  auto mfma2 = [&](int x, const bf16x8_t* fa, const bf16x8_t* fb) {
+    const int j = x >> 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = 2 * (x & 1) + h;
+      acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[j][i], 0, 0, 0);
+    }
+  };
+
+  // Epilogue: f32 accumulators -> (SwiGLU) -> bf16, rounded once; every lane
+  // issues the same buffer stores (rows past the tile and columns past N get
+  // an out-of-range offset and are dropped).
+  auto epilogue = [&](const DmaItem& x) {
+    const int cq = 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t r = (uint32_t)(wm * 128 + i * 32 + (lane & 31));
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (OP == 0) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int col = x.col0 + wn * 64 + j * 32 + 8 * g + cq;
+            float o[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float gt = acc[j][i][4 * g + v];
+              const float up = acc[j + 2][i][4 * g + v];
+              o[v] = gt * __frcp_rn(1.0f + __expf(-gt)) * up;  // silu(g) * u
+            }
+            __builtin_amdgcn_raw_buffer_store_b64(
+                int32x2_t{(int)pack_bf16x2(o[0], o[1]), (int)pack_bf16x2(o[2], o[3])}, x.rc,
+                col < N ? (r * (uint32_t)N + (uint32_t)col) * 2u : kOOB, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int col = x.col0 + wn * 128 + j * 32 + 8 * g + cq;
+            __builtin_amdgcn_raw_buffer_store_b64(
+                int32x2_t{(int)pack_bf16x2(acc[j][i][4 * g], acc[j][i][4 * g + 1]),
+                          (int)pack_bf16x2(acc[j][i][4 * g + 2], acc[j][i][4 * g + 3])},
+                x.rc, col < N ? (r * (uint32_t)N + (uint32_t)col) * 2u : kOOB, 0, 0);
+          }
+        }
+      }
+    }
+  };
+
+  int rt, ct;
+  int item = next_item((G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b, &rt, &ct);
+  DmaItem cur;
+  if (item < total) {
+    setup(rt, ct, cur);
+    issue_prologue(cur);
+  }
+  bool stores_pending = false;  // the previous item's stores were issued after these DMAs
+  while (item < total) {
+    // Slice 0 of this item: wait for this wave's DMA, then for every wave.
+    if constexpr (kDmaFirst) {
+      if (stores_pending)
+        vm_wait<2 * DMA_PER_STAGE + kStores>();
+      else
+        vm_wait<2 * DMA_PER_STAGE>();
+    } else {
+      vm_wait<2 * DMA_PER_STAGE>();
+    }
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) read_frag<OP>(x, f0a, f0b, smem_base + a_lane0, smem_base + b_lane0);
+
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint32_t cur_base = smem_base + (uint32_t)(kt & (DNSTAGE - 1)) * DSTAGE_BYTES;
+      const uint32_t nxt_base = smem_base + (uint32_t)((kt + 1) & (DNSTAGE - 1)) * DSTAGE_BYTES;
+      lgkm_wait_frags(f0a, f0b);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        read_frag<OP>(x, f1a, f1b, cur_base + a_lane1, cur_base + b_lane1);
+        mfma2(x, f0a, f0b);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      lgkm_wait_frags(f1a, f1b);
+      vm_wait<DMA_PER_STAGE>();
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        dma(cur, x, kt + 3);
+        read_frag<OP>(x, f0a, f0b, nxt_base + a_lane0, nxt_base + b_lane0);
+        mfma2(x, f1a, f1b);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // Drain the trailing (empty) DMAs and LDS reads; after the barrier no wave
+    // reads the stage buffers until the next item's slices are complete.
+    vm_wait<0>();
+    lgkm_wait_frags(f0a, f0b);
+    __builtin_amdgcn_s_barrier();
+    const int nxt = next_item(item + G, &rt, &ct);
+    DmaItem nx = cur;
+    const bool has_next = nxt < total;
+    if (has_next) setup(rt, ct, nx);
+    if (kDmaFirst && has_next) issue_prologue(nx);
+    epilogue(cur);
+    if (!kDmaFirst && has_next) issue_prologue(nx);
+    stores_pending = true;
+    item = nxt;
+    cur = nx;
+  }
+  vm_wait<0>();  // no DMA or store outlives the workgroup
+}
+
 }  // namespace
 
 moe_status_t launch_gemm_bf16(moe_gemm_op_t op, const void* a, const int32_t* offsets, int S,
@@ -365,14 +674,21 @@ moe_status_t launch_gemm_bf16(moe_gemm_op_t op, const void* a, const int32_t* of
       (ceil_div(N, BN) + 8);
   int G = device_cu_count();
   if (max_items < G) G = (int)max_items;
-  if (op == MOE_GEMM_GATE_UP_SWIGLU)
-    grouped_gemm_bf16_kernel<0><<<G, NTHR, 0, stream>>>(
-        static_cast<const uint4*>(a), offsets, S, static_cast<const uint4*>(w), N, Kd,
-        static_cast<uint16_t*>(c));
-  else
-    grouped_gemm_bf16_kernel<1><<<G, NTHR, 0, stream>>>(
-        static_cast<const uint4*>(a), offsets, S, static_cast<const uint4*>(w), N, Kd,
-        static_cast<uint16_t*>(c));
+  const uint4* a4 = static_cast<const uint4*>(a);
+  const uint4* w4 = static_cast<const uint4*>(w);
+  uint16_t* c16 = static_cast<uint16_t*>(c);
+  const bool dma = Kd % DBK == 0;
+  if (op == MOE_GEMM_GATE_UP_SWIGLU) {
+    if (dma)
+      grouped_gemm_bf16_dma_kernel<0><<<G, NTHR, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
+    else
+      grouped_gemm_bf16_kernel<0><<<G, NTHR, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
+  } else {
+    if (dma)
+      grouped_gemm_bf16_dma_kernel<1><<<G, NTHR, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
+    else
+      grouped_gemm_bf16_kernel<1><<<G, NTHR, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
+  }
   return launch_status();
 }
 
