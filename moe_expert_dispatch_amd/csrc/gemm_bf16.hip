@@ -55,7 +55,6 @@ constexpr int BK = 64;
 constexpr int BROWS = 256;  // weight rows per stage
 constexpr int NTHR = 256;
 constexpr int XCD_ITEMS = 32;  // concurrent items per XCD per round
-constexpr int DMA_PER_STAGE = 8;  // direct-to-LDS instructions per wave per K-slice
 constexpr int A_VEC = BM * BK / 8;     // 16-byte vectors per A stage (1024)
 constexpr int B_VEC = BROWS * BK / 8;  // 2048
 constexpr int STAGE_VEC = A_VEC + B_VEC;
@@ -77,18 +76,20 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
   return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
 }
 
-// Builds tp[0..S] = prefix over slots of ceil(n_s / BM) in LDS.
+// Builds tp[0..S] = prefix over slots of ceil(n_s / BM) in LDS. All NT threads
+// of the block must call it (it contains barriers); scratch holds NT ints.
+template <int NT>
 __device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int S, int32_t* tp,
                                   int32_t* scratch) {
   const int tid = threadIdx.x;
-  const int per = ceil_div(S, NTHR);
+  const int per = ceil_div(S, NT);
   const int lo = min(tid * per, S);
   const int hi = min(lo + per, S);
   int sum = 0;
   for (int s = lo; s < hi; ++s) sum += ceil_div(offsets[s + 1] - offsets[s], BM);
   scratch[tid] = sum;
   __syncthreads();
-  for (int off = 1; off < NTHR; off <<= 1) {
+  for (int off = 1; off < NT; off <<= 1) {
     const int v = tid >= off ? scratch[tid - off] : 0;
     __syncthreads();
     scratch[tid] += v;
@@ -99,7 +100,7 @@ __device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int S, in
     tp[s] = run;
     run += ceil_div(offsets[s + 1] - offsets[s], BM);
   }
-  if (tid == NTHR - 1) tp[S] = scratch[NTHR - 1];
+  if (tid == NT - 1) tp[S] = scratch[NT - 1];
   __syncthreads();
 }
 
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_kernel(
   const int GM = XCD_ITEMS / GN;
   const int nk = ceil_div(Kd, BK);
 
-  build_tile_prefix(offsets, S, tp, scan_scratch);
+  build_tile_prefix<NTHR>(offsets, S, tp, scan_scratch);
   const int RT = uniform(tp[S]);
   const int total = ceil_div(RT, GM) * GM * ceil_div(CT, GN) * GN;
 
@@ -397,39 +398,10 @@ __device__ __forceinline__ void lds_read16(bf16x8_t& d, uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF));
 }
 
-// Waits for all LDS reads and ties the fragments to the wait, so no MFMA
-// using them is scheduled above it.
-__device__ __forceinline__ void lgkm_wait_frags(bf16x8_t (&fa)[4], bf16x8_t (&fb)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]), "+v"(fb[1]),
-                 "+v"(fb[2]), "+v"(fb[3]));
-}
-
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
-}
-
-// Byte offset of weight fragment j from the lane's first weight row.
-template <int OP>
-constexpr int bfrag_off(int j) {
-  return (OP == 0 ? ((j < 2 ? 0 : BROWS / 2) + (j & 1) * 32) : j * 32) * 64;
-}
-
-template <int OP>
-__device__ __forceinline__ void read_frag(int x, bf16x8_t* fa, bf16x8_t* fb, uint32_t aa,
-                                          uint32_t ba) {
-  switch (x) {
-    case 0: lds_read16<0 * 2048>(fa[0], aa); break;
-    case 1: lds_read16<1 * 2048>(fa[1], aa); break;
-    case 2: lds_read16<2 * 2048>(fa[2], aa); break;
-    case 3: lds_read16<3 * 2048>(fa[3], aa); break;
-    case 4: lds_read16<bfrag_off<OP>(0)>(fb[0], ba); break;
-    case 5: lds_read16<bfrag_off<OP>(1)>(fb[1], ba); break;
-    case 6: lds_read16<bfrag_off<OP>(2)>(fb[2], ba); break;
-    default: lds_read16<bfrag_off<OP>(3)>(fb[3], ba); break;
-  }
 }
 
 typedef int int32x2_t __attribute__((ext_vector_type(2)));
@@ -440,25 +412,33 @@ typedef int int32x2_t __attribute__((ext_vector_type(2)));
 struct DmaItem {
   int rows, row0, col0;
   __amdgpu_buffer_rsrc_t ra, rb, rc;
-  uint32_t a_off[4], b_off[4];
+  uint32_t a_off[2], b_off[2];
 };
 
+constexpr int NTHR8 = 512;   // 8 waves: 2 per SIMD
+constexpr int DMA8 = 4;      // DMA instructions per wave per K-slice
+constexpr int DDEPTH = 3;    // K-slices issued ahead of the one being computed
+static_assert(DDEPTH >= 2 && DDEPTH <= DNSTAGE, "slice kt+DDEPTH reuses buffer of kt");
+
 template <int OP>
-__global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_dma_kernel(
+constexpr int bfrag8_off(int j) {  // byte offset of weight fragment j (0..1) of a wave
+  return (OP == 0 ? j * (BROWS / 2) : j * 32) * 64;
+}
+
+template <int OP>
+__global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
     const uint4* __restrict__ A, const int32_t* __restrict__ offsets, int S,
     const uint4* __restrict__ W, int N, int Kd, uint16_t* __restrict__ C) {
   __shared__ uint4 smem[DNSTAGE * DSTAGE_VEC];
   __shared__ int32_t tp[MOE_MAX_SLOTS + 1];
-  __shared__ int32_t scan_scratch[NTHR];
+  __shared__ int32_t scan_scratch[NTHR8];
 
-  constexpr int kStores = OP == 0 ? 32 : 64;  // epilogue store instructions per wave
-  constexpr bool kDmaFirst = 2 * DMA_PER_STAGE + kStores <= 63;
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int wave = tid / kWave;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wave = tid / kWave;  // 0..7
+  const int wm = wave >> 2;      // 128-row half of the tile
+  const int wn = wave & 3;       // quarter of the weight rows
   const size_t w_rows = (OP == 0) ? 2 * (size_t)N : (size_t)N;
   const int BN = (OP == 0) ? BROWS / 2 : BROWS;
   const int CT = ceil_div(N, BN);
@@ -467,29 +447,24 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_dma_kernel(
   const int nk = Kd / DBK;
   const uint32_t row_bytes = (uint32_t)Kd * 2u;
 
-  build_tile_prefix(offsets, S, tp, scan_scratch);
+  build_tile_prefix<NTHR8>(offsets, S, tp, scan_scratch);
   const int RT = uniform(tp[S]);
   const int total = ceil_div(RT, GM) * GM * ceil_div(CT, GN) * GN;
   const int G = gridDim.x;
   const int b = blockIdx.x;
 
-  // Fragment rows of one operand differ by multiples of 32 rows (whole swizzle
-  // periods), so every fragment address is a per-lane base for the operand
-  // and K-half plus a compile-time offset.
   const int a_row0 = wm * 128 + (lane & 31);
-  const int b_row0 = (OP == 0 ? wn * 64 : wn * 128) + (lane & 31);
+  const int b_row0 = (OP == 0 ? wn * 32 : wn * 64) + (lane & 31);
   const uint32_t a_lane0 = (uint32_t)swz4(a_row0, lane >> 5) * 16u;
   const uint32_t a_lane1 = (uint32_t)swz4(a_row0, 2 + (lane >> 5)) * 16u;
   const uint32_t b_lane0 = DA_VEC * 16u + (uint32_t)swz4(b_row0, lane >> 5) * 16u;
   const uint32_t b_lane1 = DA_VEC * 16u + (uint32_t)swz4(b_row0, 2 + (lane >> 5)) * 16u;
   const uint32_t smem_base = lds_addr(smem);
 
-  // Next valid item at or after w (block-uniform), or `total`.
   auto next_item = [&](int w, int* rt, int* ct) {
     while (w < total && !item_tile(w, RT, CT, GM, GN, rt, ct)) w += G;
     return w;
   };
-
   auto setup = [&](int rt, int ct, DmaItem& x) {
     const int s = uniform(find_slot(tp, S, rt));
     x.row0 = uniform(offsets[s] + (rt - tp[s]) * BM);
@@ -499,8 +474,8 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_dma_kernel(
     x.rb = make_rsrc(W + (size_t)s * w_rows * (Kd / 8), (uint32_t)w_rows * row_bytes);
     x.rc = make_rsrc(C + (size_t)x.row0 * N, (uint32_t)x.rows * (uint32_t)N * 2u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = wave * 4 + i;  // 16-row block of the stage
+    for (int i = 0; i < 2; ++i) {
+      const int q = wave * 2 + i;  // 16-row block of the stage
       const int r = q * 16 + (lane >> 2);
       const int ch = (lane & 3) ^ ((r >> 2) & 3);
       x.a_off[i] = (uint32_t)r * row_bytes + (uint32_t)ch * 16u;
@@ -515,44 +490,50 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_dma_kernel(
       x.b_off[i] = j < N ? (uint32_t)wrow * row_bytes + (uint32_t)ch * 16u : kOOB;
     }
   };
-  // DMA instruction q (0..7) of slice kt into its LDS stage buffer.
   auto dma = [&](const DmaItem& x, int q, int kt) {
     const int buf = kt & (DNSTAGE - 1);
     const bool live = kt < nk;
     const uint32_t kb = (uint32_t)kt * (DBK * 2);
     uint4* stage = smem + buf * DSTAGE_VEC;
-    if (q < 4) {
+    if (q < 2) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          x.ra, (lds_ptr_t)(stage + (wave * 4 + q) * 64), 16, live ? x.a_off[q] + kb : kOOB, 0,
+          x.ra, (lds_ptr_t)(stage + (wave * 2 + q) * 64), 16, live ? x.a_off[q] + kb : kOOB, 0,
           0, 0);
     } else {
-      const int i = q - 4;
+      const int i = q - 2;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          x.rb, (lds_ptr_t)(stage + DA_VEC + (wave * 4 + i) * 64), 16,
+          x.rb, (lds_ptr_t)(stage + DA_VEC + (wave * 2 + i) * 64), 16,
           (live && x.b_off[i] != kOOB) ? x.b_off[i] + kb : kOOB, 0, 0, 0);
     }
   };
   auto issue_prologue = [&](const DmaItem& x) {
 #pragma unroll
-    for (int kt = 0; kt < 3; ++kt)
+    for (int kt = 0; kt < DDEPTH; ++kt)
 #pragma unroll
-      for (int q = 0; q < DMA_PER_STAGE; ++q) dma(x, q, kt);
+      for (int q = 0; q < DMA8; ++q) dma(x, q, kt);
   };
 
-  floatx16 acc[4][4];
-  bf16x8_t f0a[4], f0b[4], f1a[4], f1b[4];
-  auto mfma2 = [&](int x, const bf16x8_t* fa, const bf16x8_t* fb) {
-    const int j = x >> 1;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int i = 2 * (x & 1) + h;
-      acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[j][i], 0, 0, 0);
+  floatx16 acc[2][4];
+  bf16x8_t f0a[4], f0b[2], f1a[4], f1b[2];
+  auto read8 = [&](int x, bf16x8_t* fa, bf16x8_t* fb, uint32_t aa, uint32_t ba) {
+    switch (x) {
+      case 0: lds_read16<0 * 2048>(fa[0], aa); break;
+      case 1: lds_read16<1 * 2048>(fa[1], aa); break;
+      case 2: lds_read16<2 * 2048>(fa[2], aa); break;
+      case 3: lds_read16<3 * 2048>(fa[3], aa); break;
+      case 4: lds_read16<bfrag8_off<OP>(0)>(fb[0], ba); break;
+      default: lds_read16<bfrag8_off<OP>(1)>(fb[1], ba); break;
     }
   };
+  auto wait_frags = [&](bf16x8_t (&fa)[4], bf16x8_t (&fb)[2]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]), "+v"(fb[1]));
+  };
+  auto mfma1 = [&](int x, const bf16x8_t* fa, const bf16x8_t* fb) {
+    const int j = x >> 2, i = x & 3;
+    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[j][i], 0, 0, 0);
+  };
 
-  // Epilogue: f32 accumulators -> (SwiGLU) -> bf16, rounded once; every lane
-  // issues the same buffer stores (rows past the tile and columns past N get
-  // an out-of-range offset and are dropped).
   auto epilogue = [&](const DmaItem& x) {
     const int cq = 4 * (lane >> 5);
 #pragma unroll
@@ -561,24 +542,21 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_dma_kernel(
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         if (OP == 0) {
+          const int col = x.col0 + wn * 32 + 8 * g + cq;
+          float o[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float gt = acc[0][i][4 * g + v];
+            const float up = acc[1][i][4 * g + v];
+            o[v] = gt * __frcp_rn(1.0f + __expf(-gt)) * up;  // silu(g) * u
+          }
+          __builtin_amdgcn_raw_buffer_store_b64(
+              int32x2_t{(int)pack_bf16x2(o[0], o[1]), (int)pack_bf16x2(o[2], o[3])}, x.rc,
+              col < N ? (r * (uint32_t)N + (uint32_t)col) * 2u : kOOB, 0, 0);
+        } else {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const int col = x.col0 + wn * 64 + j * 32 + 8 * g + cq;
-            float o[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const float gt = acc[j][i][4 * g + v];
-              const float up = acc[j + 2][i][4 * g + v];
-              o[v] = gt * __frcp_rn(1.0f + __expf(-gt)) * up;  // silu(g) * u
-            }
-            __builtin_amdgcn_raw_buffer_store_b64(
-                int32x2_t{(int)pack_bf16x2(o[0], o[1]), (int)pack_bf16x2(o[2], o[3])}, x.rc,
-                col < N ? (r * (uint32_t)N + (uint32_t)col) * 2u : kOOB, 0, 0);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int col = x.col0 + wn * 128 + j * 32 + 8 * g + cq;
             __builtin_amdgcn_raw_buffer_store_b64(
                 int32x2_t{(int)pack_bf16x2(acc[j][i][4 * g], acc[j][i][4 * g + 1]),
                           (int)pack_bf16x2(acc[j][i][4 * g + 2], acc[j][i][4 * g + 3])},
@@ -596,66 +574,53 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_dma_kernel(
     setup(rt, ct, cur);
     issue_prologue(cur);
   }
-  bool stores_pending = false;  // the previous item's stores were issued after these DMAs
   while (item < total) {
-    // Slice 0 of this item: wait for this wave's DMA, then for every wave.
-    if constexpr (kDmaFirst) {
-      if (stores_pending)
-        vm_wait<2 * DMA_PER_STAGE + kStores>();
-      else
-        vm_wait<2 * DMA_PER_STAGE>();
-    } else {
-      vm_wait<2 * DMA_PER_STAGE>();
-    }
+    vm_wait<(DDEPTH - 1) * DMA8>();
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) read_frag<OP>(x, f0a, f0b, smem_base + a_lane0, smem_base + b_lane0);
+    for (int x = 0; x < 6; ++x) read8(x, f0a, f0b, smem_base + a_lane0, smem_base + b_lane0);
 
     for (int kt = 0; kt < nk; ++kt) {
       const uint32_t cur_base = smem_base + (uint32_t)(kt & (DNSTAGE - 1)) * DSTAGE_BYTES;
       const uint32_t nxt_base = smem_base + (uint32_t)((kt + 1) & (DNSTAGE - 1)) * DSTAGE_BYTES;
-      lgkm_wait_frags(f0a, f0b);
+      wait_frags(f0a, f0b);
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        read_frag<OP>(x, f1a, f1b, cur_base + a_lane1, cur_base + b_lane1);
-        mfma2(x, f0a, f0b);
+        if (x < 6) read8(x, f1a, f1b, cur_base + a_lane1, cur_base + b_lane1);
+        mfma1(x, f0a, f0b);
         __builtin_amdgcn_sched_barrier(0);
       }
-      lgkm_wait_frags(f1a, f1b);
-      vm_wait<DMA_PER_STAGE>();
+      wait_frags(f1a, f1b);
+      vm_wait<(DDEPTH - 2) * DMA8>();
       __builtin_amdgcn_s_barrier();
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        dma(cur, x, kt + 3);
-        read_frag<OP>(x, f0a, f0b, nxt_base + a_lane0, nxt_base + b_lane0);
-        mfma2(x, f1a, f1b);
+        if (x < DMA8) dma(cur, x, kt + DDEPTH);
+        if (x < 6) read8(x, f0a, f0b, nxt_base + a_lane0, nxt_base + b_lane0);
+        mfma1(x, f1a, f1b);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 
-    // Drain the trailing (empty) DMAs and LDS reads; after the barrier no wave
-    // reads the stage buffers until the next item's slices are complete.
     vm_wait<0>();
-    lgkm_wait_frags(f0a, f0b);
+    wait_frags(f0a, f0b);
     __builtin_amdgcn_s_barrier();
     const int nxt = next_item(item + G, &rt, &ct);
     DmaItem nx = cur;
     const bool has_next = nxt < total;
     if (has_next) setup(rt, ct, nx);
-    if (kDmaFirst && has_next) issue_prologue(nx);
     epilogue(cur);
-    if (!kDmaFirst && has_next) issue_prologue(nx);
-    stores_pending = true;
+    if (has_next) issue_prologue(nx);
     item = nxt;
     cur = nx;
   }
-  vm_wait<0>();  // no DMA or store outlives the workgroup
+  vm_wait<0>();
 }
 
 }  // namespace
@@ -680,12 +645,12 @@ moe_status_t launch_gemm_bf16(moe_gemm_op_t op, const void* a, const int32_t* of
   const bool dma = Kd % DBK == 0;
   if (op == MOE_GEMM_GATE_UP_SWIGLU) {
     if (dma)
-      grouped_gemm_bf16_dma_kernel<0><<<G, NTHR, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
+      grouped_gemm_bf16_dma8_kernel<0><<<G, NTHR8, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
     else
       grouped_gemm_bf16_kernel<0><<<G, NTHR, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
   } else {
     if (dma)
-      grouped_gemm_bf16_dma_kernel<1><<<G, NTHR, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
+      grouped_gemm_bf16_dma8_kernel<1><<<G, NTHR8, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
     else
       grouped_gemm_bf16_kernel<1><<<G, NTHR, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
   }
