@@ -515,6 +515,7 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
 
   floatx16 acc[2][4];
   bf16x8_t f0a[4], f0b[2], f1a[4], f1b[2];
+  DmaItem cur;
   auto read8 = [&](int x, bf16x8_t* fa, bf16x8_t* fb, uint32_t aa, uint32_t ba) {
     switch (x) {
       case 0: lds_read16<0 * 2048>(fa[0], aa); break;
@@ -533,43 +534,82 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
     const int j = x >> 2, i = x & 3;
     acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[j][i], 0, 0, 0);
   };
+  auto mfma1_first = [&](int x, const bf16x8_t* fa, const bf16x8_t* fb) {
+    const int j = x >> 2, i = x & 3;
+    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], floatx16{}, 0, 0, 0);
+  };
 
+  // Epilogue: accumulator groups g and g+1 (4 columns each per lane half) are
+  // exchanged between the lane halves, after which lane l holds 8
+  // consecutive columns of row l mod 32 (group g for l < 32, g+1 above) and
+  // writes them as one 16-byte store.
+  auto store8 = [&](const DmaItem& x, uint32_t r, int col, const float* lo, const float* hi) {
+    uint32_t x0 = pack_bf16x2(lo[0], lo[1]), x1 = pack_bf16x2(lo[2], lo[3]);
+    uint32_t y0 = pack_bf16x2(hi[0], hi[1]), y1 = pack_bf16x2(hi[2], hi[3]);
+    const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+    __builtin_amdgcn_raw_buffer_store_b128(
+        int32x4_t{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]}, x.rc,
+        col < N ? (r * (uint32_t)N + (uint32_t)col) * 2u : kOOB, 0, 0);
+  };
   auto epilogue = [&](const DmaItem& x) {
-    const int cq = 4 * (lane >> 5);
+    const int ch = 8 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t r = (uint32_t)(wm * 128 + i * 32 + (lane & 31));
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < 4; g += 2) {
         if (OP == 0) {
-          const int col = x.col0 + wn * 32 + 8 * g + cq;
-          float o[4];
+          float o[8];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
+          for (int v = 0; v < 8; ++v) {
             const float gt = acc[0][i][4 * g + v];
             const float up = acc[1][i][4 * g + v];
-            o[v] = gt * __frcp_rn(1.0f + __expf(-gt)) * up;  // silu(g) * u
+            o[v] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;  // silu(g) * u
           }
-          __builtin_amdgcn_raw_buffer_store_b64(
-              int32x2_t{(int)pack_bf16x2(o[0], o[1]), (int)pack_bf16x2(o[2], o[3])}, x.rc,
-              col < N ? (r * (uint32_t)N + (uint32_t)col) * 2u : kOOB, 0, 0);
+          store8(x, r, x.col0 + wn * 32 + 8 * g + ch, o, o + 4);
         } else {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            const int col = x.col0 + wn * 64 + j * 32 + 8 * g + cq;
-            __builtin_amdgcn_raw_buffer_store_b64(
-                int32x2_t{(int)pack_bf16x2(acc[j][i][4 * g], acc[j][i][4 * g + 1]),
-                          (int)pack_bf16x2(acc[j][i][4 * g + 2], acc[j][i][4 * g + 3])},
-                x.rc, col < N ? (r * (uint32_t)N + (uint32_t)col) * 2u : kOOB, 0, 0);
+            float o[8];
+#pragma unroll
+            for (int v = 0; v < 8; ++v) o[v] = acc[j][i][4 * g + v];
+            store8(x, r, x.col0 + wn * 64 + j * 32 + 8 * g + ch, o, o + 4);
           }
         }
       }
     }
   };
 
+  // One K-step kt. The first step of an item starts its accumulators from
+  // zero (half 0 writes every accumulator tile once).
+  auto step = [&](int kt, auto first) {
+    const uint32_t cur_base = smem_base + (uint32_t)(kt & (DNSTAGE - 1)) * DSTAGE_BYTES;
+    const uint32_t nxt_base = smem_base + (uint32_t)((kt + 1) & (DNSTAGE - 1)) * DSTAGE_BYTES;
+    wait_frags(f0a, f0b);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      if (x < 6) read8(x, f1a, f1b, cur_base + a_lane1, cur_base + b_lane1);
+      if constexpr (decltype(first)::value)
+        mfma1_first(x, f0a, f0b);
+      else
+        mfma1(x, f0a, f0b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_frags(f1a, f1b);
+    vm_wait<(DDEPTH - 2) * DMA8>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      if (x < DMA8) dma(cur, x, kt + DDEPTH);
+      if (x < 6) read8(x, f0a, f0b, nxt_base + a_lane0, nxt_base + b_lane0);
+      mfma1(x, f1a, f1b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   int rt, ct;
   int item = next_item((G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b, &rt, &ct);
-  DmaItem cur;
   if (item < total) {
     setup(rt, ct, cur);
     issue_prologue(cur);
@@ -578,47 +618,24 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
     vm_wait<(DDEPTH - 1) * DMA8>();
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
-#pragma unroll
     for (int x = 0; x < 6; ++x) read8(x, f0a, f0b, smem_base + a_lane0, smem_base + b_lane0);
 
-    for (int kt = 0; kt < nk; ++kt) {
-      const uint32_t cur_base = smem_base + (uint32_t)(kt & (DNSTAGE - 1)) * DSTAGE_BYTES;
-      const uint32_t nxt_base = smem_base + (uint32_t)((kt + 1) & (DNSTAGE - 1)) * DSTAGE_BYTES;
-      wait_frags(f0a, f0b);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        if (x < 6) read8(x, f1a, f1b, cur_base + a_lane1, cur_base + b_lane1);
-        mfma1(x, f0a, f0b);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      wait_frags(f1a, f1b);
-      vm_wait<(DDEPTH - 2) * DMA8>();
-      __builtin_amdgcn_s_barrier();
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        if (x < DMA8) dma(cur, x, kt + DDEPTH);
-        if (x < 6) read8(x, f0a, f0b, nxt_base + a_lane0, nxt_base + b_lane0);
-        mfma1(x, f1a, f1b);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+    step(0, std::true_type{});
+    int kt = 1;
+    do {  // nk >= DDEPTH > 1
+      step(kt, std::false_type{});
+    } while (++kt < nk);
 
     vm_wait<0>();
     wait_frags(f0a, f0b);
     __builtin_amdgcn_s_barrier();
     const int nxt = next_item(item + G, &rt, &ct);
-    DmaItem nx = cur;
+    DmaItem done = cur;
     const bool has_next = nxt < total;
-    if (has_next) setup(rt, ct, nx);
-    epilogue(cur);
-    if (has_next) issue_prologue(nx);
+    if (has_next) setup(rt, ct, cur);
+    epilogue(done);
+    if (has_next) issue_prologue(cur);
     item = nxt;
-    cur = nx;
   }
   vm_wait<0>();
 }
@@ -642,7 +659,9 @@ moe_status_t launch_gemm_bf16(moe_gemm_op_t op, const void* a, const int32_t* of
   const uint4* a4 = static_cast<const uint4*>(a);
   const uint4* w4 = static_cast<const uint4*>(w);
   uint16_t* c16 = static_cast<uint16_t*>(c);
-  const bool dma = Kd % DBK == 0;
+  // The direct-to-LDS kernel needs whole 32-wide K-slices and at least
+  // DDEPTH of them.
+  const bool dma = Kd % DBK == 0 && Kd >= DDEPTH * DBK;
   if (op == MOE_GEMM_GATE_UP_SWIGLU) {
     if (dma)
       grouped_gemm_bf16_dma8_kernel<0><<<G, NTHR8, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
