@@ -184,7 +184,15 @@ def main():
     gemm_tflops = (fl_gu + fl_dn) / ((stage_ms["gemm_gate_up"] + stage_ms["gemm_down"]) * 1e9)
     gu_tflops = fl_gu / (stage_ms["gemm_gate_up"] * 1e9)
     P = cfg.T * cfg.K
-    permute_bytes = cfg.T * cfg.H * eb + P_in * cfg.H * eb + 9 * P + 12 * P
+    # Permutation: count and scatter each read slot + mask (5 B per pair), the
+    # scatter writes pair_row (4 B per pair) and sorted_pairs (4 B per included
+    # pair). For bf16 with H a multiple of 32 (>= 96) the row gather is folded
+    # into the gate/up GEMM; otherwise permute also copies the rows.
+    fused_gather = cfg.dtype == "bf16" and cfg.H % 32 == 0 and cfg.H >= 96 \
+        and cfg.T * cfg.H * 2 < 2 ** 31
+    permute_bytes = 2 * 5 * P + 4 * P + 4 * P_in
+    if not fused_gather:
+        permute_bytes += cfg.T * cfg.H * eb + P_in * cfg.H * eb
     combine_bytes = P_in * cfg.H * eb + 8 * P + cfg.T * cfg.H * eb
     traffic = gemm_traffic()
 

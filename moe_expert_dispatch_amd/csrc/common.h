@@ -88,6 +88,15 @@ moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
 moe_status_t launch_gemm_bf16(moe_gemm_op_t op, const void* a, const int32_t* offsets, int S,
                               int max_rows, const void* w, int H, int I, void* c,
                               hipStream_t stream);
+// Gate/up product with the permutation's gather folded into the operand fetch:
+// row r of the permuted order is token sorted_pairs[r] / K of x [T, H]. Only
+// for shapes where gemm_bf16_gather_ok(T, H) holds.
+bool gemm_bf16_gather_ok(int T, int H);
+moe_status_t launch_gemm_bf16_gate_up_gathered(const void* x, int T, int K,
+                                               const int32_t* sorted_pairs,
+                                               const int32_t* offsets, int S, int max_rows,
+                                               const void* w, int H, int I, void* c,
+                                               hipStream_t stream);
 moe_status_t launch_gemm_f32(moe_gemm_op_t op, const void* a, const int32_t* offsets, int S,
                              int max_rows, const void* w, int H, int I, void* c,
                              hipStream_t stream);

@@ -425,10 +425,14 @@ constexpr int bfrag8_off(int j) {  // byte offset of weight fragment j (0..1) of
   return (OP == 0 ? j * (BROWS / 2) : j * 32) * 64;
 }
 
-template <int OP>
+// GATHER: activation row r of the permuted order is row gather[r] / topk of A
+// (A has a_rows rows), i.e. the permutation's gather is folded into the
+// operand fetch. Otherwise A is already in permuted order.
+template <int OP, bool GATHER>
 __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
     const uint4* __restrict__ A, const int32_t* __restrict__ offsets, int S,
-    const uint4* __restrict__ W, int N, int Kd, uint16_t* __restrict__ C) {
+    const uint4* __restrict__ W, int N, int Kd, uint16_t* __restrict__ C,
+    const int32_t* __restrict__ gather, int topk, int a_rows) {
   __shared__ uint4 smem[DNSTAGE * DSTAGE_VEC];
   __shared__ int32_t tp[MOE_MAX_SLOTS + 1];
   __shared__ int32_t scan_scratch[NTHR8];
@@ -470,7 +474,10 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
     x.row0 = uniform(offsets[s] + (rt - tp[s]) * BM);
     x.rows = uniform(min(BM, offsets[s + 1] - x.row0));
     x.col0 = ct * BN;
-    x.ra = make_rsrc(A + (size_t)x.row0 * (Kd / 8), (uint32_t)x.rows * row_bytes);
+    if constexpr (GATHER)
+      x.ra = make_rsrc(A, (uint32_t)a_rows * row_bytes);
+    else
+      x.ra = make_rsrc(A + (size_t)x.row0 * (Kd / 8), (uint32_t)x.rows * row_bytes);
     x.rb = make_rsrc(W + (size_t)s * w_rows * (Kd / 8), (uint32_t)w_rows * row_bytes);
     x.rc = make_rsrc(C + (size_t)x.row0 * N, (uint32_t)x.rows * (uint32_t)N * 2u);
 #pragma unroll
@@ -478,7 +485,10 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
       const int q = wave * 2 + i;  // 16-row block of the stage
       const int r = q * 16 + (lane >> 2);
       const int ch = (lane & 3) ^ ((r >> 2) & 3);
-      x.a_off[i] = (uint32_t)r * row_bytes + (uint32_t)ch * 16u;
+      if constexpr (GATHER)  // pair index for now; gather_offsets() finishes it
+        x.a_off[i] = r < x.rows ? (uint32_t)gather[x.row0 + r] : kOOB;
+      else
+        x.a_off[i] = (uint32_t)r * row_bytes + (uint32_t)ch * 16u;
       int j, wrow;
       if (OP == 0) {
         j = x.col0 + (r & (BROWS / 2 - 1));
@@ -488,6 +498,20 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
         wrow = j;
       }
       x.b_off[i] = j < N ? (uint32_t)wrow * row_bytes + (uint32_t)ch * 16u : kOOB;
+    }
+  };
+  // Pair index -> byte offset of its token's row (the index loads were issued
+  // by setup, so their latency overlaps whatever ran in between).
+  auto gather_offsets = [&](DmaItem& x) {
+    if constexpr (GATHER) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = (wave * 2 + i) * 16 + (lane >> 2);
+        const int ch = (lane & 3) ^ ((r >> 2) & 3);
+        x.a_off[i] = x.a_off[i] != kOOB
+                         ? (x.a_off[i] / (uint32_t)topk) * row_bytes + (uint32_t)ch * 16u
+                         : kOOB;
+      }
     }
   };
   auto dma = [&](const DmaItem& x, int q, int kt) {
@@ -612,6 +636,7 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
   int item = next_item((G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b, &rt, &ct);
   if (item < total) {
     setup(rt, ct, cur);
+    gather_offsets(cur);
     issue_prologue(cur);
   }
   while (item < total) {
@@ -634,11 +659,32 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
     const bool has_next = nxt < total;
     if (has_next) setup(rt, ct, cur);
     epilogue(done);
-    if (has_next) issue_prologue(cur);
+    if (has_next) {
+      gather_offsets(cur);
+      issue_prologue(cur);
+    }
     item = nxt;
   }
   vm_wait<0>();
 }
+
+}  // namespace
+
+namespace {
+
+int gemm_grid(int max_rows, int S, int N, int BN) {
+  // Upper bound on items: sum_s ceil(n_s/BM) <= ceil(max_rows/BM) + min(S, max_rows),
+  // plus the holes of partial item groups.
+  const long long max_items =
+      (long long)(ceil_div(max_rows, BM) + (S < max_rows ? S : max_rows) + XCD_ITEMS) *
+      (ceil_div(N, BN) + 8);
+  const int G = device_cu_count();
+  return max_items < G ? (int)max_items : G;
+}
+
+// The direct-to-LDS kernel needs whole 32-wide K-slices and at least DDEPTH
+// of them.
+bool dma_ok(int Kd) { return Kd % DBK == 0 && Kd >= DDEPTH * DBK; }
 
 }  // namespace
 
@@ -649,30 +695,43 @@ moe_status_t launch_gemm_bf16(moe_gemm_op_t op, const void* a, const int32_t* of
   const int N = (op == MOE_GEMM_GATE_UP_SWIGLU) ? I : H;
   const int Kd = (op == MOE_GEMM_GATE_UP_SWIGLU) ? H : I;
   const int BN = (op == MOE_GEMM_GATE_UP_SWIGLU) ? BROWS / 2 : BROWS;
-  // Upper bound on items: sum_s ceil(n_s/BM) <= ceil(max_rows/BM) + min(S, max_rows),
-  // plus the holes of partial item groups.
-  const long long max_items =
-      (long long)(ceil_div(max_rows, BM) + (S < max_rows ? S : max_rows) + XCD_ITEMS) *
-      (ceil_div(N, BN) + 8);
-  int G = device_cu_count();
-  if (max_items < G) G = (int)max_items;
+  const int G = gemm_grid(max_rows, S, N, BN);
   const uint4* a4 = static_cast<const uint4*>(a);
   const uint4* w4 = static_cast<const uint4*>(w);
   uint16_t* c16 = static_cast<uint16_t*>(c);
-  // The direct-to-LDS kernel needs whole 32-wide K-slices and at least
-  // DDEPTH of them.
-  const bool dma = Kd % DBK == 0 && Kd >= DDEPTH * DBK;
+  const bool dma = dma_ok(Kd);
   if (op == MOE_GEMM_GATE_UP_SWIGLU) {
     if (dma)
-      grouped_gemm_bf16_dma8_kernel<0><<<G, NTHR8, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
+      grouped_gemm_bf16_dma8_kernel<0, false>
+          <<<G, NTHR8, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16, nullptr, 1, 0);
     else
       grouped_gemm_bf16_kernel<0><<<G, NTHR, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
   } else {
     if (dma)
-      grouped_gemm_bf16_dma8_kernel<1><<<G, NTHR8, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
+      grouped_gemm_bf16_dma8_kernel<1, false>
+          <<<G, NTHR8, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16, nullptr, 1, 0);
     else
       grouped_gemm_bf16_kernel<1><<<G, NTHR, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
   }
+  return launch_status();
+}
+
+bool gemm_bf16_gather_ok(int T, int H) {
+  // Every byte offset into x, plus the out-of-range marker, fits 32 bits.
+  return dma_ok(H) && (size_t)T * (size_t)H * 2u < (size_t)kOOB;
+}
+
+moe_status_t launch_gemm_bf16_gate_up_gathered(const void* x, int T, int K,
+                                               const int32_t* sorted_pairs,
+                                               const int32_t* offsets, int S, int max_rows,
+                                               const void* w, int H, int I, void* c,
+                                               hipStream_t stream) {
+  if (!gemm_bf16_gather_ok(T, H)) return MOE_ERR_UNSUPPORTED;
+  if (max_rows == 0) return MOE_OK;
+  const int G = gemm_grid(max_rows, S, I, BROWS / 2);
+  grouped_gemm_bf16_dma8_kernel<0, true><<<G, NTHR8, 0, stream>>>(
+      static_cast<const uint4*>(x), offsets, S, static_cast<const uint4*>(w), I, H,
+      static_cast<uint16_t*>(c), sorted_pairs, K, T);
   return launch_status();
 }
 

@@ -294,11 +294,19 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_forward_args_t* args
   MOE_TRY(launch_slot_map(ids_in, w_in, T, K, cfg->ep_rank * E_local, E_local, args->rep_off,
                           args->rep_slots, S, slot, w_masked, mask, stream));
   MOE_TRY(mark(MOE_EV_ROUTED));
+  // bf16 with a direct-to-LDS shape: the gate/up GEMM fetches token rows of x
+  // itself, so the permutation only orders the pairs (no x_perm copy).
+  const bool fused_gather = cfg->dtype == MOE_DTYPE_BF16 && gemm_bf16_gather_ok(T, H);
   MOE_TRY(launch_permute(args->x, dtype_bytes(cfg->dtype), T, H, K, slot, mask, S, offsets,
-                         sorted_pairs, pair_row, x_perm, perm_ws, stream));
+                         sorted_pairs, pair_row, fused_gather ? nullptr : x_perm, perm_ws,
+                         stream));
   MOE_TRY(mark(MOE_EV_PERMUTED));
-  MOE_TRY(launch_gemm(MOE_GEMM_GATE_UP_SWIGLU, cfg->dtype, x_perm, offsets, S, T * K,
-                      args->w_gate_up, H, I, act, stream));
+  if (fused_gather)
+    MOE_TRY(launch_gemm_bf16_gate_up_gathered(args->x, T, K, sorted_pairs, offsets, S, T * K,
+                                              args->w_gate_up, H, I, act, stream));
+  else
+    MOE_TRY(launch_gemm(MOE_GEMM_GATE_UP_SWIGLU, cfg->dtype, x_perm, offsets, S, T * K,
+                        args->w_gate_up, H, I, act, stream));
   MOE_TRY(mark(MOE_EV_GATE_UP));
   MOE_TRY(launch_gemm(MOE_GEMM_DOWN, cfg->dtype, act, offsets, S, T * K, args->w_down, H, I, y,
                       stream));

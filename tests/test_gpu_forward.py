@@ -306,9 +306,12 @@ def test_determinism_and_topk_form(dev):
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
-def test_forward_matches_staged_calls(dev):
-    """moe_forward is the staged entry points in sequence: same bits."""
-    inp = _medium("bf16_ragged")
+@pytest.mark.parametrize("name", ["bf16_ragged", "bf16_odd_dims"])
+def test_forward_matches_staged_calls(dev, name):
+    """moe_forward gives the bits of the staged entry points in sequence, both
+    where it folds the row gather into the gate/up GEMM (H = 256) and where
+    it runs the permutation's gather (H = 136, not a multiple of 32)."""
+    inp = _medium(name)
     cfg = inp.cfg
     wgu, wd, ro, rs, S = share_tensors(inp, dev)
     announce("forward vs staged")
