@@ -13,11 +13,16 @@
 // `offsets`, so slots with no rows produce no items and no host readback of
 // the row counts is needed.
 //
-// Tiles: BM = 256 rows x 256 weight rows x BK = 64, 256 threads (4 waves in
-// a 2 x 2 layout, 128 x 128 per wave). For the gate/up product the 256
-// weight rows are 128 gate rows and the matching 128 up rows, so each block
-// produces a 256 x 128 tile of silu(G) * U without ever storing G or U. For
-// the down product they are 256 output columns. Both operands are
+// Two kernels share the tiling, item order and epilogue math: a
+// direct-to-LDS kernel (further below) for K a multiple of 64 (K >= 128),
+// and a register-staged kernel for every other K (a multiple of 8).
+//
+// Tiles: BM = 256 rows x 256 weight rows. Register-staged kernel: BK = 64,
+// 256 threads (4 waves in a 2 x 2 layout, 128 x 128 per wave). For the
+// gate/up product the 256 weight rows are 128 gate rows and the matching 128
+// up rows, so each block produces a 256 x 128 tile of silu(G) * U without
+// ever storing G or U. For the down product they are 256 output columns.
+// Both operands are
 // K-contiguous in HBM and in LDS; LDS rows are 128 bytes with the 16-byte
 // chunks XOR-swizzled by (row mod 8), which keeps the MFMA fragment reads
 // free of bank conflicts. Two LDS stages: the next K-slice is fetched into
@@ -353,41 +358,43 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS variant, used when K % 32 == 0. Same tiles, item order and
-// epilogue, with BK = 32 and four LDS stages of 32 KB filled by
-// buffer_load_dwordx4 ... lds: no registers hold prefetched data, so three
-// K-slices (96 KB per CU) are in flight while one is computed on.
+// Direct-to-LDS kernel, used when K % 64 == 0 and K >= 128. Same tiles, item
+// order and SwiGLU as above, with 8 waves (two per SIMD, so each SIMD has two
+// instruction streams) in a 2 x 4 layout of 128 x 64 wave tiles, and the
+// operands moved by buffer_load_dwordx4 ... lds: no registers hold
+// prefetched data.
 //
-// LDS rows are 64 bytes; the 16-byte chunk c of row r sits at c ^ ((r>>2)&3),
-// which keeps the 32-row fragment reads conflict-free. One DMA instruction
-// fills 1 KB of LDS linearly (lane L writes bytes 16L..16L+15), i.e. 16 rows x
-// 4 chunks, so lane L fetches the global chunk that belongs at that position.
+// LDS holds two buffers of one 64-wide K-slice each (64 KB: 256 activation
+// rows and 256 weight rows of 128 bytes). Chunk c of row r sits at
+// c ^ ((r >> 1) & 7), which keeps the 32-row fragment reads free of bank
+// conflicts. One DMA instruction fills 1 KB of LDS linearly (lane L writes
+// bytes 16L..16L+15), i.e. 8 whole rows, so lane L fetches the global chunk
+// that belongs at that position and every request is a full 128-byte line.
 //
-// The fragment reads are issued as inline ds_read_b128 with explicit
-// lgkmcnt waits, and the DMA completion with explicit vmcnt waits: the
-// compiler's own tracking of LDS DMA would otherwise drain every pending
-// slice before each LDS read. Per K-step kt (buffer kt&3):
-//   half 0: MFMAs on K-16 block 0 (fragments in registers), each pair
-//           followed by one LDS read of block 1;
-//   wait:   block-1 reads complete; this wave's DMA of slice kt+1 complete
-//           (vmcnt <= 8: only slice kt+2 may be pending); workgroup barrier,
-//           after which slice kt+1 is complete for every wave and buffer
-//           (kt-1)&3 is no longer read by anyone;
-//   half 1: MFMAs on block 1, each pair with one DMA instruction of slice
-//           kt+3 (into buffer (kt+3)&3 = (kt-1)&3) and one LDS read of
-//           block 0 of slice kt+1.
-// Every step issues the same 8 DMA instructions per wave (slices past the
+// The fragment reads are inline ds_read_b128 with explicit lgkmcnt waits, and
+// DMA completion uses explicit vmcnt waits: the compiler's own tracking of
+// LDS DMA would otherwise drain every pending load before each LDS read. Per
+// slice d (buffer d & 1), in four K-16 blocks:
+//   blocks 0-2: MFMAs on block kb (fragments in registers), each followed by
+//               one LDS read of block kb+1;
+//   wait:       block-3 reads complete; this wave's DMA of slice d+1
+//               complete (vmcnt 0); workgroup barrier, after which slice d+1
+//               is complete for every wave and buffer d & 1 is not read by
+//               anyone;
+//   block 3:    MFMAs, each with one DMA instruction of slice d+2 (into
+//               buffer d & 1) and one LDS read of block 0 of slice d+1.
+// Every slice issues the same 8 DMA instructions per wave (slices past the
 // end use an out-of-range offset and move nothing), so the vmcnt accounting
-// is constant. The epilogue uses buffer stores with a fixed instruction
-// count; the next item's first three slices are issued before or after them
-// so that the wait for slice 0 stays within the 6-bit vmcnt.
-constexpr int DBK = 32;
-constexpr int DA_VEC = BM * DBK / 8;                 // 1024 vectors: A part of a stage
-constexpr int DSTAGE_VEC = (BM + BROWS) * DBK / 8;   // 2048 vectors = 32 KB
-constexpr int DSTAGE_BYTES = DSTAGE_VEC * 16;
-constexpr int DNSTAGE = 4;
+// is constant. An item's epilogue stores are issued before the next item's
+// first two slices, so the wait for slice 0 also covers them.
+constexpr int NTHR8 = 512;  // 8 waves: 2 per SIMD
+constexpr int WBK = 64;
+constexpr int WA_VEC = BM * WBK / 8;                // 2048 vectors: A part of a stage
+constexpr int WSTAGE_VEC = (BM + BROWS) * WBK / 8;  // 4096 vectors = 64 KB
+constexpr int WSTAGE_BYTES = WSTAGE_VEC * 16;
+constexpr int WDMA = 8;  // DMA instructions per wave per slice
 
-__device__ __forceinline__ int swz4(int row, int ch) { return row * 4 + (ch ^ ((row >> 2) & 3)); }
+__device__ __forceinline__ int wswz(int row, int ch) { return row * 8 + (ch ^ ((row >> 1) & 7)); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -404,36 +411,23 @@ __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
 }
 
-typedef int int32x2_t __attribute__((ext_vector_type(2)));
-
-// One item of the direct-to-LDS kernel: tile geometry, buffer descriptors of
-// the activation rows, the weight panel and the output rows, and this lane's
-// DMA source offsets.
-struct DmaItem {
-  int rows, row0, col0;
-  __amdgpu_buffer_rsrc_t ra, rb, rc;
-  uint32_t a_off[2], b_off[2];
-};
-
-constexpr int NTHR8 = 512;   // 8 waves: 2 per SIMD
-constexpr int DMA8 = 4;      // DMA instructions per wave per K-slice
-constexpr int DDEPTH = 3;    // K-slices issued ahead of the one being computed
-static_assert(DDEPTH >= 2 && DDEPTH <= DNSTAGE, "slice kt+DDEPTH reuses buffer of kt");
-
 template <int OP>
-constexpr int bfrag8_off(int j) {  // byte offset of weight fragment j (0..1) of a wave
-  return (OP == 0 ? j * (BROWS / 2) : j * 32) * 64;
+constexpr int bfragw_off(int j) {  // byte offset of weight fragment j (0..1) of a wave
+  return (OP == 0 ? j * (BROWS / 2) : j * 32) * 128;
 }
 
-// GATHER: activation row r of the permuted order is row gather[r] / topk of A
-// (A has a_rows rows), i.e. the permutation's gather is folded into the
-// operand fetch. Otherwise A is already in permuted order.
+struct WItem {
+  int rows, row0, col0;
+  __amdgpu_buffer_rsrc_t ra, rb, rc;
+  uint32_t a_off[4], b_off[4];
+};
+
 template <int OP, bool GATHER>
-__global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
+__global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma_kernel(
     const uint4* __restrict__ A, const int32_t* __restrict__ offsets, int S,
     const uint4* __restrict__ W, int N, int Kd, uint16_t* __restrict__ C,
     const int32_t* __restrict__ gather, int topk, int a_rows) {
-  __shared__ uint4 smem[DNSTAGE * DSTAGE_VEC];
+  __shared__ uint4 smem[2 * WSTAGE_VEC];
   __shared__ int32_t tp[MOE_MAX_SLOTS + 1];
   __shared__ int32_t scan_scratch[NTHR8];
 
@@ -448,7 +442,7 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
   const int CT = ceil_div(N, BN);
   const int GN = CT < 8 ? CT : 8;
   const int GM = XCD_ITEMS / GN;
-  const int nk = Kd / DBK;
+  const int nd = Kd / WBK;  // K-slices
   const uint32_t row_bytes = (uint32_t)Kd * 2u;
 
   build_tile_prefix<NTHR8>(offsets, S, tp, scan_scratch);
@@ -459,17 +453,20 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
 
   const int a_row0 = wm * 128 + (lane & 31);
   const int b_row0 = (OP == 0 ? wn * 32 : wn * 64) + (lane & 31);
-  const uint32_t a_lane0 = (uint32_t)swz4(a_row0, lane >> 5) * 16u;
-  const uint32_t a_lane1 = (uint32_t)swz4(a_row0, 2 + (lane >> 5)) * 16u;
-  const uint32_t b_lane0 = DA_VEC * 16u + (uint32_t)swz4(b_row0, lane >> 5) * 16u;
-  const uint32_t b_lane1 = DA_VEC * 16u + (uint32_t)swz4(b_row0, 2 + (lane >> 5)) * 16u;
+  // Lane offsets of K-16 block kb of the lane's first A and B fragment rows.
+  uint32_t a_lane[4], b_lane[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    a_lane[kb] = (uint32_t)wswz(a_row0, 2 * kb + (lane >> 5)) * 16u;
+    b_lane[kb] = WA_VEC * 16u + (uint32_t)wswz(b_row0, 2 * kb + (lane >> 5)) * 16u;
+  }
   const uint32_t smem_base = lds_addr(smem);
 
   auto next_item = [&](int w, int* rt, int* ct) {
     while (w < total && !item_tile(w, RT, CT, GM, GN, rt, ct)) w += G;
     return w;
   };
-  auto setup = [&](int rt, int ct, DmaItem& x) {
+  auto setup = [&](int rt, int ct, WItem& x) {
     const int s = uniform(find_slot(tp, S, rt));
     x.row0 = uniform(offsets[s] + (rt - tp[s]) * BM);
     x.rows = uniform(min(BM, offsets[s + 1] - x.row0));
@@ -481,10 +478,10 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
     x.rb = make_rsrc(W + (size_t)s * w_rows * (Kd / 8), (uint32_t)w_rows * row_bytes);
     x.rc = make_rsrc(C + (size_t)x.row0 * N, (uint32_t)x.rows * (uint32_t)N * 2u);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = wave * 2 + i;  // 16-row block of the stage
-      const int r = q * 16 + (lane >> 2);
-      const int ch = (lane & 3) ^ ((r >> 2) & 3);
+    for (int i = 0; i < 4; ++i) {
+      const int q = wave * 4 + i;  // 8-row block of the stage
+      const int r = q * 8 + (lane >> 3);
+      const int ch = (lane & 7) ^ ((r >> 1) & 7);
       if constexpr (GATHER)  // pair index for now; gather_offsets() finishes it
         x.a_off[i] = r < x.rows ? (uint32_t)gather[x.row0 + r] : kOOB;
       else
@@ -502,52 +499,53 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
   };
   // Pair index -> byte offset of its token's row (the index loads were issued
   // by setup, so their latency overlaps whatever ran in between).
-  auto gather_offsets = [&](DmaItem& x) {
+  auto gather_offsets = [&](WItem& x) {
     if constexpr (GATHER) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = (wave * 2 + i) * 16 + (lane >> 2);
-        const int ch = (lane & 3) ^ ((r >> 2) & 3);
+      for (int i = 0; i < 4; ++i) {
+        const int r = (wave * 4 + i) * 8 + (lane >> 3);
+        const int ch = (lane & 7) ^ ((r >> 1) & 7);
         x.a_off[i] = x.a_off[i] != kOOB
                          ? (x.a_off[i] / (uint32_t)topk) * row_bytes + (uint32_t)ch * 16u
                          : kOOB;
       }
     }
   };
-  auto dma = [&](const DmaItem& x, int q, int kt) {
-    const int buf = kt & (DNSTAGE - 1);
-    const bool live = kt < nk;
-    const uint32_t kb = (uint32_t)kt * (DBK * 2);
-    uint4* stage = smem + buf * DSTAGE_VEC;
-    if (q < 2) {
+  // DMA instruction q (0..7) of slice d into buffer d & 1: 8 rows x 128
+  // bytes, i.e. whole cache lines.
+  auto dma = [&](const WItem& x, int q, int d) {
+    const bool live = d < nd;
+    const uint32_t kb = (uint32_t)d * (WBK * 2);
+    uint4* stage = smem + (d & 1) * WSTAGE_VEC;
+    if (q < 4) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          x.ra, (lds_ptr_t)(stage + (wave * 2 + q) * 64), 16, live ? x.a_off[q] + kb : kOOB, 0,
+          x.ra, (lds_ptr_t)(stage + (wave * 4 + q) * 64), 16, live ? x.a_off[q] + kb : kOOB, 0,
           0, 0);
     } else {
-      const int i = q - 2;
+      const int i = q - 4;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          x.rb, (lds_ptr_t)(stage + DA_VEC + (wave * 2 + i) * 64), 16,
+          x.rb, (lds_ptr_t)(stage + WA_VEC + (wave * 4 + i) * 64), 16,
           (live && x.b_off[i] != kOOB) ? x.b_off[i] + kb : kOOB, 0, 0, 0);
     }
   };
-  auto issue_prologue = [&](const DmaItem& x) {
+  auto issue_prologue = [&](const WItem& x) {
 #pragma unroll
-    for (int kt = 0; kt < DDEPTH; ++kt)
+    for (int d = 0; d < 2; ++d)
 #pragma unroll
-      for (int q = 0; q < DMA8; ++q) dma(x, q, kt);
+      for (int q = 0; q < WDMA; ++q) dma(x, q, d);
   };
 
   floatx16 acc[2][4];
   bf16x8_t f0a[4], f0b[2], f1a[4], f1b[2];
-  DmaItem cur;
+  WItem cur;
   auto read8 = [&](int x, bf16x8_t* fa, bf16x8_t* fb, uint32_t aa, uint32_t ba) {
     switch (x) {
-      case 0: lds_read16<0 * 2048>(fa[0], aa); break;
-      case 1: lds_read16<1 * 2048>(fa[1], aa); break;
-      case 2: lds_read16<2 * 2048>(fa[2], aa); break;
-      case 3: lds_read16<3 * 2048>(fa[3], aa); break;
-      case 4: lds_read16<bfrag8_off<OP>(0)>(fb[0], ba); break;
-      default: lds_read16<bfrag8_off<OP>(1)>(fb[1], ba); break;
+      case 0: lds_read16<0 * 4096>(fa[0], aa); break;
+      case 1: lds_read16<1 * 4096>(fa[1], aa); break;
+      case 2: lds_read16<2 * 4096>(fa[2], aa); break;
+      case 3: lds_read16<3 * 4096>(fa[3], aa); break;
+      case 4: lds_read16<bfragw_off<OP>(0)>(fb[0], ba); break;
+      default: lds_read16<bfragw_off<OP>(1)>(fb[1], ba); break;
     }
   };
   auto wait_frags = [&](bf16x8_t (&fa)[4], bf16x8_t (&fb)[2]) {
@@ -567,7 +565,7 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
   // exchanged between the lane halves, after which lane l holds 8
   // consecutive columns of row l mod 32 (group g for l < 32, g+1 above) and
   // writes them as one 16-byte store.
-  auto store8 = [&](const DmaItem& x, uint32_t r, int col, const float* lo, const float* hi) {
+  auto store8 = [&](const WItem& x, uint32_t r, int col, const float* lo, const float* hi) {
     uint32_t x0 = pack_bf16x2(lo[0], lo[1]), x1 = pack_bf16x2(lo[2], lo[3]);
     uint32_t y0 = pack_bf16x2(hi[0], hi[1]), y1 = pack_bf16x2(hi[2], hi[3]);
     const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
@@ -576,7 +574,7 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
         int32x4_t{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]}, x.rc,
         col < N ? (r * (uint32_t)N + (uint32_t)col) * 2u : kOOB, 0, 0);
   };
-  auto epilogue = [&](const DmaItem& x) {
+  auto epilogue = [&](const WItem& x) {
     const int ch = 8 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -605,15 +603,18 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
     }
   };
 
-  // One K-step kt. The first step of an item starts its accumulators from
-  // zero (half 0 writes every accumulator tile once).
-  auto step = [&](int kt, auto first) {
-    const uint32_t cur_base = smem_base + (uint32_t)(kt & (DNSTAGE - 1)) * DSTAGE_BYTES;
-    const uint32_t nxt_base = smem_base + (uint32_t)((kt + 1) & (DNSTAGE - 1)) * DSTAGE_BYTES;
+  // One K-slice d = four K-16 blocks. Block kb+1 is read while block kb
+  // is computed; before the last block, this wave's DMA of slice d+1 is
+  // waited for and the workgroup synchronises, after which slice d+1 is
+  // visible everywhere and buffer d & 1 is no longer read, so the DMA of
+  // slice d+2 goes there while block 0 of slice d+1 is read.
+  auto dstep = [&](int d, auto first) {
+    const uint32_t base = smem_base + (uint32_t)(d & 1) * WSTAGE_BYTES;
+    const uint32_t nbase = smem_base + (uint32_t)((d + 1) & 1) * WSTAGE_BYTES;
     wait_frags(f0a, f0b);
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-      if (x < 6) read8(x, f1a, f1b, cur_base + a_lane1, cur_base + b_lane1);
+      if (x < 6) read8(x, f1a, f1b, base + a_lane[1], base + b_lane[1]);
       if constexpr (decltype(first)::value)
         mfma1_first(x, f0a, f0b);
       else
@@ -621,12 +622,26 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_frags(f1a, f1b);
-    vm_wait<(DDEPTH - 2) * DMA8>();
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      if (x < 6) read8(x, f0a, f0b, base + a_lane[2], base + b_lane[2]);
+      mfma1(x, f1a, f1b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_frags(f0a, f0b);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      if (x < 6) read8(x, f1a, f1b, base + a_lane[3], base + b_lane[3]);
+      mfma1(x, f0a, f0b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_frags(f1a, f1b);
+    vm_wait<0>();
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-      if (x < DMA8) dma(cur, x, kt + DDEPTH);
-      if (x < 6) read8(x, f0a, f0b, nxt_base + a_lane0, nxt_base + b_lane0);
+      dma(cur, x, d + 2);
+      if (x < 6) read8(x, f0a, f0b, nbase + a_lane[0], nbase + b_lane[0]);
       mfma1(x, f1a, f1b);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -640,22 +655,19 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma8_kernel(
     issue_prologue(cur);
   }
   while (item < total) {
-    vm_wait<(DDEPTH - 1) * DMA8>();
+    vm_wait<WDMA>();
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int x = 0; x < 6; ++x) read8(x, f0a, f0b, smem_base + a_lane0, smem_base + b_lane0);
+    for (int x = 0; x < 6; ++x) read8(x, f0a, f0b, smem_base + a_lane[0], smem_base + b_lane[0]);
 
-    step(0, std::true_type{});
-    int kt = 1;
-    do {  // nk >= DDEPTH > 1
-      step(kt, std::false_type{});
-    } while (++kt < nk);
+    dstep(0, std::true_type{});
+    for (int d = 1; d < nd; ++d) dstep(d, std::false_type{});
 
     vm_wait<0>();
     wait_frags(f0a, f0b);
     __builtin_amdgcn_s_barrier();
     const int nxt = next_item(item + G, &rt, &ct);
-    DmaItem done = cur;
+    WItem done = cur;
     const bool has_next = nxt < total;
     if (has_next) setup(rt, ct, cur);
     epilogue(done);
@@ -682,9 +694,8 @@ int gemm_grid(int max_rows, int S, int N, int BN) {
   return max_items < G ? (int)max_items : G;
 }
 
-// The direct-to-LDS kernel needs whole 32-wide K-slices and at least DDEPTH
-// of them.
-bool dma_ok(int Kd) { return Kd % DBK == 0 && Kd >= DDEPTH * DBK; }
+// The direct-to-LDS kernel needs whole 64-wide K-slices, at least two.
+bool dma_ok(int Kd) { return Kd % WBK == 0 && Kd >= 2 * WBK; }
 
 }  // namespace
 
@@ -702,13 +713,13 @@ moe_status_t launch_gemm_bf16(moe_gemm_op_t op, const void* a, const int32_t* of
   const bool dma = dma_ok(Kd);
   if (op == MOE_GEMM_GATE_UP_SWIGLU) {
     if (dma)
-      grouped_gemm_bf16_dma8_kernel<0, false>
+      grouped_gemm_bf16_dma_kernel<0, false>
           <<<G, NTHR8, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16, nullptr, 1, 0);
     else
       grouped_gemm_bf16_kernel<0><<<G, NTHR, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
   } else {
     if (dma)
-      grouped_gemm_bf16_dma8_kernel<1, false>
+      grouped_gemm_bf16_dma_kernel<1, false>
           <<<G, NTHR8, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16, nullptr, 1, 0);
     else
       grouped_gemm_bf16_kernel<1><<<G, NTHR, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
@@ -729,7 +740,7 @@ moe_status_t launch_gemm_bf16_gate_up_gathered(const void* x, int T, int K,
   if (!gemm_bf16_gather_ok(T, H)) return MOE_ERR_UNSUPPORTED;
   if (max_rows == 0) return MOE_OK;
   const int G = gemm_grid(max_rows, S, I, BROWS / 2);
-  grouped_gemm_bf16_dma8_kernel<0, true><<<G, NTHR8, 0, stream>>>(
+  grouped_gemm_bf16_dma_kernel<0, true><<<G, NTHR8, 0, stream>>>(
       static_cast<const uint4*>(x), offsets, S, static_cast<const uint4*>(w), I, H,
       static_cast<uint16_t*>(c), sorted_pairs, K, T);
   return launch_status();
