@@ -10,6 +10,7 @@ from __future__ import annotations
 import concurrent.futures as _fut
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -42,7 +43,38 @@ COMPILE_FLAGS = [
 ]
 
 
-def _run(cmd, verbose):
+# The direct-to-LDS GEMM counts its own outstanding vector-memory operations
+# (s_waitcnt vmcnt with fixed counts), so no compiler-generated memory access
+# may appear in it: register spills to scratch would shift every count. The
+# build asks for the resource-usage remarks and rejects such a kernel (file ->
+# kernel-name fragment) if it uses scratch.
+NO_SCRATCH = {"gemm_bf16.hip": "grouped_gemm_bf16_dma_kernel"}
+_REMARK = "kernel-resource-usage"
+
+
+_SCRATCH = re.compile(r"(ScratchSize \[bytes/lane\]|VGPRs Spill): (\d+)")
+
+
+def _check_no_scratch(src, out):
+    frag = NO_SCRATCH[os.path.basename(src)]
+    name = None
+    for line in out.splitlines():
+        if _REMARK not in line:
+            continue
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = _SCRATCH.search(line)
+        if m and name and frag in name and int(m.group(2)) != 0:
+            raise RuntimeError(f"{os.path.basename(src)}: kernel {name} reports "
+                               f"{m.group(1)} {m.group(2)}; its hand-counted memory waits "
+                               "need a kernel without scratch accesses")
+
+
+def _run(cmd, verbose, check_src=None):
+    if check_src:
+        cmd = [*cmd, f"-Rpass-analysis={_REMARK}"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -50,6 +82,10 @@ def _run(cmd, verbose):
                     if "packed-fp32-ops' is not a recognized feature" not in l)
     if res.returncode != 0:
         raise RuntimeError(f"command failed ({res.returncode}): {' '.join(cmd)}\n{out}")
+    if check_src:
+        _check_no_scratch(check_src, out)
+        if not verbose:
+            out = ""
     if verbose and out.strip():
         print(out, flush=True)
 
@@ -63,7 +99,8 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     objs = [os.path.join(BUILD_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
     jobs = jobs or min(len(srcs), os.cpu_count() or 1, 16)
     with _fut.ThreadPoolExecutor(jobs) as ex:
-        futs = [ex.submit(_run, [cc, *COMPILE_FLAGS, "-c", s, "-o", o], verbose)
+        futs = [ex.submit(_run, [cc, *COMPILE_FLAGS, "-c", s, "-o", o], verbose,
+                          s if os.path.basename(s) in NO_SCRATCH else None)
                 for s, o in zip(srcs, objs)]
         for f in futs:
             f.result()
