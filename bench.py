@@ -186,9 +186,9 @@ def main():
     P = cfg.T * cfg.K
     # Permutation: count and scatter each read slot + mask (5 B per pair), the
     # scatter writes pair_row (4 B per pair) and sorted_pairs (4 B per included
-    # pair). For bf16 with H a multiple of 32 (>= 96) the row gather is folded
+    # pair). For bf16 with H a multiple of 64 (>= 128) the row gather is folded
     # into the gate/up GEMM; otherwise permute also copies the rows.
-    fused_gather = cfg.dtype == "bf16" and cfg.H % 32 == 0 and cfg.H >= 96 \
+    fused_gather = cfg.dtype == "bf16" and cfg.H % 64 == 0 and cfg.H >= 128 \
         and cfg.T * cfg.H * 2 < 2 ** 31
     permute_bytes = 2 * 5 * P + 4 * P + 4 * P_in
     if not fused_gather:
