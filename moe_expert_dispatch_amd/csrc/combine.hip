@@ -15,6 +15,38 @@
 namespace moe {
 namespace {
 
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kVec = 2;  // 8-element vectors per thread
+
+// Buffer resource over one row of Y: [row, row + bytes). A resource of 0
+// bytes (an excluded pair) makes every load return zeros without a memory
+// access, so the loads need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ void load8(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint16_t*,
+                                      float* v) {
+  const int32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32((uint32_t)q[i] & 0xffffu);
+    v[2 * i + 1] = bf16_to_f32((uint32_t)q[i] >> 16);
+  }
+}
+
+__device__ __forceinline__ void load8(__amdgpu_buffer_rsrc_t r, uint32_t off, const float*,
+                                      float* v) {
+  const int32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  const int32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16u), 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = __int_as_float(a[i]);
+    v[4 + i] = __int_as_float(b[i]);
+  }
+}
+
 __device__ __forceinline__ void load8(const uint16_t* p, float* v) {
   const uint4 q = *reinterpret_cast<const uint4*>(p);
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -46,7 +78,12 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-template <typename YT, typename OT>
+// One block per token. Each thread owns kVec vectors of 8 elements. The K
+// row loads of both vectors are issued before any arithmetic (each through
+// a resource over its own row, empty for an excluded pair), which keeps
+// K * kVec loads in flight per thread; the included pairs are then added in
+// ascending k.
+template <typename YT, typename OT, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
                                                       const int32_t* __restrict__ pair_row,
                                                       const float* __restrict__ w_masked, int K,
@@ -61,33 +98,60 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
   }
   __syncthreads();
   const int nvec = H / 8;
+  const uint32_t row_bytes = (uint32_t)H * (uint32_t)sizeof(YT);
   OT* o = out + (size_t)t * H;
-  for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < K; ++k) {
-      const int r = rows[k];
-      if (r < 0) continue;
-      const float wk = wts[k];
-      float yv[8];
-      load8(y + (size_t)r * H + v * 8, yv);
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += kVec * blockDim.x) {
+    float acc[kVec][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(wk, yv[i], acc[i]);
-    }
-    if (accumulate) {
-      float prev[8];
-      load8(o + v * 8, prev);
+    for (int u = 0; u < kVec; ++u)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = prev[i] + acc[i];
+      for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
+    for (int k0 = 0; k0 < K; k0 += KMAX) {
+      float yv[KMAX][kVec][8];
+#pragma unroll
+      for (int kk = 0; kk < KMAX; ++kk) {
+        const int r = k0 + kk < K ? rows[k0 + kk] : -1;
+        const __amdgpu_buffer_rsrc_t rr =
+            row_rsrc(y + (size_t)(r >= 0 ? r : 0) * H, r >= 0 ? row_bytes : 0u);
+#pragma unroll
+        for (int u = 0; u < kVec; ++u) {
+          const int v = v0 + u * blockDim.x;
+          load8(rr, v < nvec ? (uint32_t)v * 8u * (uint32_t)sizeof(YT) : row_bytes, y,
+                yv[kk][u]);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < KMAX; ++kk) {
+        const int k = k0 + kk;
+        if (k < K && rows[k] >= 0) {
+          const float wk = wts[k];
+#pragma unroll
+          for (int u = 0; u < kVec; ++u)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[u][i] = fmaf(wk, yv[kk][u][i], acc[u][i]);
+        }
+      }
     }
-    store8(o + v * 8, acc);
+#pragma unroll
+    for (int u = 0; u < kVec; ++u) {
+      const int v = v0 + u * blockDim.x;
+      if (v >= nvec) continue;
+      if (accumulate) {
+        float prev[8];
+        load8(o + v * 8, prev);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[u][i] = prev[i] + acc[u][i];
+      }
+      store8(o + v * 8, acc[u]);
+    }
   }
 }
 
 template <typename YT, typename OT>
 void launch_typed(const void* y, const int32_t* pair_row, const float* w_masked, int T, int K,
                   int H, void* out, int accumulate, hipStream_t stream) {
-  combine_kernel<YT, OT><<<T, 256, 0, stream>>>(static_cast<const YT*>(y), pair_row, w_masked,
-                                                K, H, static_cast<OT*>(out), accumulate);
+  combine_kernel<YT, OT, 8><<<T, 256, 0, stream>>>(static_cast<const YT*>(y), pair_row, w_masked,
+                                                   K, H, static_cast<OT*>(out), accumulate);
 }
 
 }  // namespace
