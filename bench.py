@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused-MoE layer tokens/sec; grouped-GEMM TFLOP/s as % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3  # MI355X fp32 vector (FMA) peak
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_traffic.json")
 GEMM_SRC = os.path.join(ROOT, "moe_expert_dispatch_amd", "csrc", "gemm_bf16.hip")
@@ -45,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--ep-rank", type=int, default=0,
+                    help="expert-parallel share to time (workloads with ep_size > 1)")
     return ap.parse_args()
 
 
@@ -60,22 +63,23 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
 
 
-def gemm_traffic():
+def gemm_traffic(workload):
     """HBM traffic of grouped GEMM 1 from the committed profiler summary, or
-    None if the kernel source changed since the counters were taken."""
+    None if the kernel source changed since the counters were taken or they
+    were taken on another workload."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
         with open(GEMM_SRC, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
-        if rec.get("kernel_source_sha256") != sha:
+        if rec.get("kernel_source_sha256") != sha or rec.get("workload") != workload:
             return None
         return rec.get("bytes_per_launch")
     except (OSError, ValueError):
         return None
 
 
-def cpu_baseline(inp, seconds):
+def cpu_baseline(inp, seconds, rank=0):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -89,7 +93,7 @@ def cpu_baseline(inp, seconds):
     while True:
         tok = np.arange(done, min(done + block, cfg.T))
         oracle.forward(inp.x, inp.logits, inp.w_gate_up, inp.w_down, cfg.K, cfg.renormalize,
-                       cfg.ep_size, 0, tokens=tok)
+                       cfg.ep_size, rank, tokens=tok)
         done += tok.size
         el = time.perf_counter() - t0
         if el >= seconds or done >= cfg.T:
@@ -119,18 +123,22 @@ def main():
     moe.lib()
     dev = torch.device("cuda:0")
     cfg = CONFIGS[args.workload]
+    rank = args.ep_rank
+    if not 0 <= rank < cfg.ep_size:
+        print(f"--ep-rank must be in [0, {cfg.ep_size}) for {cfg.name}", file=sys.stderr)
+        sys.exit(2)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     t_gen = time.perf_counter()
     inp = make_inputs(cfg)
     if cfg.n_replicated:
         ro, rs, se = build_slot_table(cfg.E_local, inp.replicated_experts())
-        wgu_h, wd_h = inp.share_weights(0)
+        wgu_h, wd_h = inp.share_weights(rank)
         wgu = slot_weights(wgu_h, se).to(dev)
         wd = slot_weights(wd_h, se).to(dev)
         S = int(se.numel())
     else:
         ro, rs = identity_slot_table(cfg.E_local)
-        wgu_h, wd_h = inp.share_weights(0)
+        wgu_h, wd_h = inp.share_weights(rank)
         wgu, wd = wgu_h.contiguous().to(dev), wd_h.contiguous().to(dev)
         S = cfg.E_local
     x = inp.x.to(dev)
@@ -140,13 +148,13 @@ def main():
 
     fc = moe.ForwardConfig(T=cfg.T, H=cfg.H, I=cfg.I, E_global=cfg.E, K=cfg.K,
                            renormalize=cfg.renormalize, S=S, dtype=tdt, ep_size=cfg.ep_size,
-                           ep_rank=0)
+                           ep_rank=rank)
     ws = torch.empty(moe.forward_workspace_size(fc), dtype=torch.uint8, device=dev)
     out = torch.empty(cfg.T, cfg.H, dtype=tdt, device=dev)
 
     # included pairs of this batch (all pairs when ep_size == 1)
     ids, w = moe.route(logits, cfg.K, cfg.renormalize)
-    slot, wm, mask = moe.slot_map(ids, w, cfg.E, cfg.ep_size, 0, ro, rs)
+    slot, wm, mask = moe.slot_map(ids, w, cfg.E, cfg.ep_size, rank, ro, rs)
     P_in = int(mask.sum().item())
 
     def step(events=None):
@@ -194,7 +202,16 @@ def main():
     if not fused_gather:
         permute_bytes += cfg.T * cfg.H * eb + P_in * cfg.H * eb
     combine_bytes = P_in * cfg.H * eb + 8 * P + cfg.T * cfg.H * eb
-    traffic = gemm_traffic()
+    # GEMM floor: the larger of the compute time at peak and the time to stream
+    # every slot's weights plus the activations (x or x_perm read, A written and
+    # read, Y written) at HBM peak.
+    peak_tf = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    gemm_bytes = (S * 3 * cfg.H * cfg.I * eb
+                  + (cfg.T if fused_gather else P_in) * cfg.H * eb
+                  + 2 * P_in * cfg.I * eb + P_in * cfg.H * eb)
+    gemm_floor_ms = max((fl_gu + fl_dn) / (peak_tf * 1e9), gemm_bytes / (PEAK_HBM_GBPS * 1e6))
+    gemm_ms = stage_ms["gemm_gate_up"] + stage_ms["gemm_down"]
+    traffic = gemm_traffic(cfg.name) if cfg.dtype == "bf16" else None
 
     res = {
         "metric": METRIC,
@@ -211,13 +228,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H,
                    "intermediate": cfg.I, "experts": cfg.E, "slots": S, "top_k": cfg.K,
-                   "renormalize": cfg.renormalize, "ep_size": cfg.ep_size,
+                   "renormalize": cfg.renormalize, "ep_size": cfg.ep_size, "ep_rank": rank,
                    "included_pairs": P_in, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_bf16 gate/up + SwiGLU",
-                     "achieved": gu_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": gu_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
+        "roofline": ({"bound": "mfma", "kernel": "grouped_gemm_bf16 gate/up + SwiGLU",
+                      "achieved": gu_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                      "frac": gu_tflops / PEAK_BF16_TFLOPS, "traffic": traffic}
+                     if cfg.dtype == "bf16" else
+                     {"bound": "alu", "kernel": "grouped_gemm_f32 gate/up + SwiGLU (FMA)",
+                      "achieved": gu_tflops, "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                      "frac": gu_tflops / PEAK_F32_TFLOPS, "traffic": None}),
         "grouped_gemm_tflops": gemm_tflops,
         "grouped_gemm_frac_of_bf16_peak": gemm_tflops / PEAK_BF16_TFLOPS,
+        "grouped_gemm_floor_ms": gemm_floor_ms,
+        "grouped_gemm_frac_of_roofline": gemm_floor_ms / gemm_ms,
         "stage_ms": stage_ms,
         "permute_gbps": permute_bytes / (stage_ms["permute"] * 1e6),
         "combine_gbps": combine_bytes / (stage_ms["combine"] * 1e6),
@@ -225,7 +248,7 @@ def main():
         "input_generation_s": gen_s,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, rank)
     print(json.dumps(res), flush=True)
 
 
