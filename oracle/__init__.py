@@ -4,6 +4,8 @@ TEST INFRASTRUCTURE: imported only by the tests, the smoke check and the
 benchmark's CPU-baseline leg. The HIP library never imports it.
 """
 from .moe_oracle import (  # noqa: F401
+    a2a_dispatch_indices,
+    a2a_forward,
     combine_rows,
     ep_mask_and_remap,
     ep_partition,

@@ -165,6 +165,60 @@ def permute_rows(x: np.ndarray, sorted_pairs, K: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# All-to-all dispatch. [A2A] walkthrough sequence diagram: the fused op sends
+# tokens to the ranks responsible for their experts, each rank computes the
+# MoE on its local experts, and the results are gathered back; the mapping
+# configuration's max-num-tokens field sizes the exchange workspace.
+# Readings: a token goes once to every rank that owns at least one of its K
+# experts (owner of e = e // E_local), carrying its full routing; rank r's
+# block holds at most max-num-tokens rows and starts at row r * cap; inside
+# a block tokens keep ascending index; the gathered result of a token is the
+# sum of the ranks' partial outputs in ascending rank order.
+# --------------------------------------------------------------------------
+def a2a_dispatch_indices(ids, E_global: int, ep_size: int, cap: int):
+    """(counts [ep], send_token [ep*cap] (-1 where unused), token_pos [T, ep]
+    (row of token t in rank r's block, or -1))."""
+    ids = _i64(ids)
+    T = ids.shape[0]
+    E_local, _ = ep_partition(E_global, ep_size, 0)
+    valid = (ids >= 0) & (ids < E_global)
+    owner = np.where(valid, ids // E_local, -1)
+    counts = np.zeros(ep_size, dtype=np.int64)
+    send_token = np.full(ep_size * cap, -1, dtype=np.int64)
+    token_pos = np.full((T, ep_size), -1, dtype=np.int64)
+    for r in range(ep_size):
+        toks = np.nonzero((owner == r).any(axis=1))[0]
+        assert toks.size <= cap, "rank block over capacity"
+        counts[r] = toks.size
+        rows = r * cap + np.arange(toks.size)
+        send_token[rows] = toks
+        token_pos[toks, r] = rows
+    return counts.astype(np.int32), send_token.astype(np.int32), token_pos.astype(np.int32)
+
+
+def a2a_forward(x, ids, w, w_gate_up, w_down, E_global: int, ep_size: int, cap: int):
+    """Dispatch, per-rank expert compute on the received tokens (each rank
+    masks to its own experts), and the gather-sum back to token order."""
+    x64 = _f64(x)
+    T, H = x64.shape
+    K = np.asarray(ids).shape[1]
+    counts, send_token, token_pos = a2a_dispatch_indices(ids, E_global, ep_size, cap)
+    partial = np.zeros((ep_size * cap, H))
+    for r in range(ep_size):
+        rows = r * cap + np.arange(int(counts[r]))
+        toks = _i64(send_token[rows])
+        if toks.size == 0:
+            continue
+        partial[rows] = forward(x64[toks], None, w_gate_up, w_down, K, False, ep_size, r,
+                                topk=(_i64(ids)[toks], _f64(w)[toks]))
+    out = np.zeros((T, H))
+    for r in range(ep_size):  # ascending rank
+        has = token_pos[:, r] >= 0
+        out[has] += partial[_i64(token_pos[has, r])]
+    return out
+
+
+# --------------------------------------------------------------------------
 # Expert MLP. [A2A] review of torch_moe.py: gated MLP with an activation
 # function; SwiGLU is the gate taken here: silu(z) = z / (1 + exp(-z)).
 # --------------------------------------------------------------------------

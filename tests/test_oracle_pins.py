@@ -216,6 +216,92 @@ def test_permute_bruteforce_and_invariants(seed):
 
 
 # ---------------------------------------------------------------- MLP / forward
+def test_a2a_dispatch_golden_vectors():
+    for c in load_golden("a2a_dispatch.json")["cases"]:
+        counts, send_token, token_pos = oracle.a2a_dispatch_indices(
+            np.array(c["ids"]), c["E_global"], c["ep_size"], c["cap"])
+        assert counts.tolist() == c["counts"], c["name"]
+        assert send_token.tolist() == c["send_token"], c["name"]
+        assert token_pos.tolist() == c["token_pos"], c["name"]
+
+
+def _a2a_bruteforce(ids, E_global, ep_size, cap):
+    """Scalar loops: for each rank, walk the tokens in order and append a token
+    the first time one of its experts belongs to that rank."""
+    T, K = len(ids), len(ids[0])
+    E_local = E_global // ep_size
+    counts = [0] * ep_size
+    send_token = [-1] * (ep_size * cap)
+    token_pos = [[-1] * ep_size for _ in range(T)]
+    for r in range(ep_size):
+        for t in range(T):
+            mine = False
+            for k in range(K):
+                e = int(ids[t][k])
+                if 0 <= e < E_global and r * E_local <= e < (r + 1) * E_local:
+                    mine = True
+            if mine:
+                row = r * cap + counts[r]
+                send_token[row] = t
+                token_pos[t][r] = row
+                counts[r] += 1
+    return counts, send_token, token_pos
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_a2a_dispatch_bruteforce(seed):
+    rng = np.random.default_rng(100 + seed)
+    E, ep = [(8, 2), (16, 4), (12, 3), (32, 8), (6, 1)][seed]
+    T, K = 37, min(4, E)
+    ids = np.stack([rng.choice(E, K, replace=False) for _ in range(T)])
+    ids[rng.random((T, K)) < 0.05] = -1  # invalid ids go nowhere
+    cap = T
+    got = oracle.a2a_dispatch_indices(ids, E, ep, cap)
+    want = _a2a_bruteforce(ids.tolist(), E, ep, cap)
+    assert got[0].tolist() == want[0]
+    assert got[1].tolist() == want[1]
+    assert got[2].tolist() == want[2]
+    # each token reaches exactly the ranks owning its valid experts
+    E_l = E // ep
+    for t in range(T):
+        owners = {int(e) // E_l for e in ids[t] if 0 <= e < E}
+        assert {r for r in range(ep) if got[2][t, r] >= 0} == owners
+
+
+@pytest.mark.parametrize("ep_size", [1, 2, 4])
+def test_a2a_forward_equals_full_forward(ep_size):
+    """Dispatch + per-rank local compute + gather-sum is the full layer: each
+    pair is computed on exactly one rank (its expert's owner) and the ranks'
+    partial sums add up; only the summation order differs."""
+    rng = np.random.default_rng(7 + ep_size)
+    T, H, I, E, K = 19, 16, 24, 8, 3
+    x = rng.standard_normal((T, H))
+    logits = rng.standard_normal((T, E))
+    wgu = rng.standard_normal((E, 2 * I, H)) / 4
+    wd = rng.standard_normal((E, H, I)) / 5
+    ids, w = oracle.route(logits, K, True)
+    full = oracle.forward(x, logits, wgu, wd, K, True)
+    a2a = oracle.a2a_forward(x, ids, w, wgu, wd, E, ep_size, cap=T)
+    np.testing.assert_allclose(a2a, full, rtol=1e-12, atol=1e-12)
+
+
+def test_mutation_a2a_owner_rule_is_caught(monkeypatch):
+    # planted mistake: experts dealt to ranks round-robin (owner e % ep_size)
+    # instead of in contiguous ranges
+    orig = om.a2a_dispatch_indices
+
+    def bad_dispatch(ids, E_global, ep_size, cap):
+        ids = np.asarray(ids)
+        E_l = E_global // ep_size
+        perm = (ids % ep_size) * E_l + ids // ep_size
+        return orig(np.where(ids >= 0, perm, ids), E_global, ep_size, cap)
+
+    monkeypatch.setattr(om, "a2a_dispatch_indices", bad_dispatch)
+    monkeypatch.setattr(oracle, "a2a_dispatch_indices", bad_dispatch)
+    with pytest.raises(AssertionError):
+        test_a2a_dispatch_golden_vectors()
+
+
 def test_silu_matches_torch():
     z = np.linspace(-30, 30, 1001)
     np.testing.assert_allclose(oracle.silu(z), F.silu(torch.as_tensor(z)).numpy(),
