@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--a2a", action="store_true",
+                    help="time the all-to-all dispatch path on an expert-parallel workload")
     ap.add_argument("--ep-rank", type=int, default=0,
                     help="expert-parallel share to time (workloads with ep_size > 1)")
     return ap.parse_args()
@@ -61,6 +63,78 @@ def copy_probe():
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+
+
+def run_a2a(args):
+    """All-to-all path of an expert-parallel workload on one GPU: dispatch to
+    ep_size blocks, each rank's fused forward over its block (f32 partials),
+    gather-sum. Prints one JSON line (not the layer's headline metric)."""
+    import torch
+
+    import moe_expert_dispatch_amd as moe
+    from workloads import CONFIGS, make_inputs
+
+    moe.lib()
+    dev = torch.device("cuda:0")
+    name = args.workload if CONFIGS[args.workload].ep_size > 1 else "ep_share_256_bf16"
+    cfg = CONFIGS[name]
+    R, T, El = cfg.ep_size, cfg.T, cfg.E_local
+    inp = make_inputs(cfg)
+    x = inp.x.to(dev)
+    ids, w = moe.route(inp.logits.to(dev), cfg.K, cfg.renormalize)
+    wgu = [inp.w_gate_up[r * El:(r + 1) * El].contiguous().to(dev) for r in range(R)]
+    wd = [inp.w_down[r * El:(r + 1) * El].contiguous().to(dev) for r in range(R)]
+    fc = [moe.ForwardConfig(T=T, H=cfg.H, I=cfg.I, E_global=cfg.E, K=cfg.K, renormalize=False,
+                            S=El, dtype=torch.bfloat16, out_dtype=torch.float32, ep_size=R,
+                            ep_rank=r) for r in range(R)]
+    fws = torch.empty(moe.forward_workspace_size(fc[0]), dtype=torch.uint8, device=dev)
+    dws = torch.empty(max(moe.a2a_dispatch_workspace_size(T, R, T), 1), dtype=torch.uint8,
+                      device=dev)
+    partial = torch.empty(R * T, cfg.H, dtype=torch.float32, device=dev)
+    state = {}
+
+    def dispatch():
+        state["d"] = moe.a2a_dispatch(x, ids, w, cfg.E, R, T, ws=dws)
+
+    def experts():
+        _, _, _, sx, sids, sw = state["d"]
+        for r in range(R):
+            blk = slice(r * T, (r + 1) * T)
+            moe.forward(fc[r], sx[blk], wgu[r], wd[r], topk_ids=sids[blk], topk_w=sw[blk],
+                        out=partial[blk], ws=fws)
+
+    def gather():
+        state["out"] = moe.a2a_combine(partial, state["d"][1], out_dtype=torch.bfloat16)
+
+    for _ in range(args.warmup):
+        dispatch(); experts(); gather()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record(); dispatch(); e[1].record(); experts(); e[2].record(); gather(); e[3].record()
+    torch.cuda.synchronize()
+    t_d = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    t_x = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    t_g = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    sent = int((state["d"][1] >= 0).sum().item())  # (token, rank) messages
+    eb = 2
+    # dispatch: read each token row once, write one row per message, plus the
+    # routing copied with it and the index arrays
+    d_bytes = T * cfg.H * eb + sent * cfg.H * eb + R * T * cfg.K * 8 + T * R * 9 + T * cfg.K * 4
+    g_bytes = sent * cfg.H * 4 + T * cfg.H * eb + T * R * 4
+    step = t_d + t_x + t_g
+    res = {"metric": "all-to-all expert-parallel layer tokens/sec (dispatch, per-rank experts, "
+                     "gather-sum; one GPU)",
+           "value": T / (step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": step, "higher_is_better": True,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": name, "tokens": T, "hidden": cfg.H, "experts": cfg.E,
+                      "top_k": cfg.K, "ranks": R, "messages": sent},
+           "stage_ms": {"dispatch": t_d, "rank_forwards": t_x, "gather_sum": t_g},
+           "dispatch_gbps": d_bytes / (t_d * 1e6), "gather_sum_gbps": g_bytes / (t_g * 1e6),
+           "dispatch_frac_of_hbm": d_bytes / (t_d * 1e6) / PEAK_HBM_GBPS,
+           "gather_sum_frac_of_hbm": g_bytes / (t_g * 1e6) / PEAK_HBM_GBPS}
+    print(json.dumps(res), flush=True)
 
 
 def gemm_traffic(workload):
@@ -119,6 +193,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.a2a:
+        run_a2a(args)
         return
     moe.lib()
     dev = torch.device("cuda:0")

@@ -83,6 +83,7 @@ typedef enum {
 #define MOE_MAX_EXPERTS 1024 /* E_global */
 #define MOE_MAX_TOPK 32      /* K */
 #define MOE_MAX_SLOTS 1024   /* S */
+#define MOE_MAX_A2A_RANKS 32 /* ep_size of the all-to-all dispatch */
 
 /* Human-readable name of a status code (static storage). */
 const char* moe_status_str(moe_status_t status);
@@ -259,6 +260,52 @@ typedef struct {
 size_t moe_forward_workspace_size(const moe_config_t* cfg);
 moe_status_t moe_forward(const moe_config_t* cfg, const moe_forward_args_t* args, void* ws,
                          size_t ws_bytes, hipStream_t stream);
+
+/*
+ * All-to-all dispatch of expert parallelism (send and return side on one
+ * device; the transport between ranks is not part of this library).
+ *   Source: [A2A] walkthrough sequence diagram: tokens are dispatched to the
+ *   ranks responsible for their experts, each rank computes the MoE on its
+ *   local experts and the results are gathered back; the mapping
+ *   configuration's max-num-tokens field sizes the exchange workspace.
+ *   [EPMASK] _ep_init: rank r owns experts [r*E_l, (r+1)*E_l), E_l =
+ *   E_global / ep_size.
+ *
+ * moe_a2a_dispatch packs the send buffers. A token t goes once to every rank
+ * that owns at least one of its valid experts (0 <= topk_ids[t*K+k] <
+ * E_global); rank r's block is rows [r*cap, (r+1)*cap) of the send arrays,
+ * tokens in ascending order. cap >= T is required (a block then never
+ * overflows; size it by the largest token count, as the max-num-tokens field
+ * does). Outputs (bit-exact):
+ *   offsets [ep_size + 1]: offsets[r] = tokens sent to ranks < r (so rank r
+ *     receives offsets[r+1] - offsets[r] tokens);
+ *   token_pos [T * ep_size]: the send row of token t for rank r, or -1;
+ *   send_token [ep_size * cap]: the token in each row, or -1 if unused;
+ *   send_x [ep_size * cap, H] (dtype dt): send_x[row] = x[send_token[row]]
+ *     bit for bit (unused rows untouched);
+ *   send_ids, send_w [ep_size * cap, K]: the token's topk_ids / topk_w, or
+ *     -1 / 0 in unused rows, so a receiving moe_forward over the whole block
+ *     (topk form, its own ep_rank) excludes the unused rows.
+ * x, send_x: H * sizeof(dt) a multiple of 16 bytes, 16-byte aligned.
+ * ws: at least moe_a2a_dispatch_workspace_size(T, ep_size, cap) bytes.
+ * Limits: 1 <= ep_size <= MOE_MAX_A2A_RANKS, E_global % ep_size == 0,
+ * 1 <= K <= MOE_MAX_TOPK.
+ *
+ * moe_a2a_combine gathers the ranks' partial outputs back into token order:
+ *   out[t] = round(sum over r = 0..ep_size-1 ascending with
+ *                  token_pos[t*ep_size + r] >= 0 of partial[token_pos[...]])
+ * with f32 accumulation and one rounding to out_dt. partial [ep_size*cap, H]
+ * of partial_dt (f32 keeps the single rounding); tokens sent nowhere give 0.
+ */
+size_t moe_a2a_dispatch_workspace_size(int T, int ep_size, int cap);
+moe_status_t moe_a2a_dispatch(const void* x, moe_dtype_t dt, int T, int H, int K,
+                              const int32_t* topk_ids, const float* topk_w, int E_global,
+                              int ep_size, int cap, int32_t* offsets, int32_t* token_pos,
+                              int32_t* send_token, void* send_x, int32_t* send_ids,
+                              float* send_w, void* ws, size_t ws_bytes, hipStream_t stream);
+moe_status_t moe_a2a_combine(const void* partial, moe_dtype_t partial_dt,
+                             const int32_t* token_pos, int T, int ep_size, int H, void* out,
+                             moe_dtype_t out_dt, hipStream_t stream);
 
 #ifdef __cplusplus
 }

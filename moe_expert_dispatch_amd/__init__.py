@@ -23,6 +23,7 @@ __all__ = [
     "lib", "library_path", "status_str",
     "route", "slot_map", "permute", "permute_workspace_size", "grouped_gemm", "combine",
     "forward", "forward_workspace_size", "ForwardConfig",
+    "a2a_dispatch", "a2a_dispatch_workspace_size", "a2a_combine",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +68,10 @@ _SIGS = {
     "moe_combine": (_i, [_p, _i, _p, _p, _i, _i, _i, _p, _i, _i, _p]),
     "moe_forward_workspace_size": (_sz, [ctypes.POINTER(_Config)]),
     "moe_forward": (_i, [ctypes.POINTER(_Config), ctypes.POINTER(_ForwardArgs), _p, _sz, _p]),
+    "moe_a2a_dispatch_workspace_size": (_sz, [_i, _i, _i]),
+    "moe_a2a_dispatch": (_i, [_p, _i, _i, _i, _i, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _p,
+                              _p, _sz, _p]),
+    "moe_a2a_combine": (_i, [_p, _i, _p, _i, _i, _i, _p, _i, _p]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -326,4 +331,54 @@ def forward(cfg: ForwardConfig, x: torch.Tensor, w_gate_up: torch.Tensor, w_down
     c = cfg.c_struct()
     _check(lib().moe_forward(ctypes.byref(c), ctypes.byref(args), _ptr(ws),
                              ws.numel() * ws.element_size(), _stream()), "moe_forward")
+    return out
+
+
+# ---------------------------------------------------------------- all-to-all
+def a2a_dispatch_workspace_size(T: int, ep_size: int, cap: int) -> int:
+    return int(lib().moe_a2a_dispatch_workspace_size(T, ep_size, cap))
+
+
+def a2a_dispatch(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, E_global: int,
+                 ep_size: int, cap: Optional[int] = None, ws: Optional[torch.Tensor] = None):
+    """moe_a2a_dispatch -> (offsets [ep+1], token_pos [T, ep], send_token [ep*cap],
+    send_x [ep*cap, H], send_ids [ep*cap, K], send_w [ep*cap, K]).
+
+    Rank r's block is rows [r*cap, (r+1)*cap); cap defaults to T."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    _dev(topk_ids, "topk_ids", torch.int32)
+    T, K = topk_ids.shape
+    _dev(topk_w, "topk_w", torch.float32, (T, K))
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be [T, H] with T matching topk_ids")
+    H = x.shape[1]
+    cap = T if cap is None else cap
+    offsets = _empty((ep_size + 1,), torch.int32, x)
+    token_pos = _empty((T, ep_size), torch.int32, x)
+    send_token = _empty((ep_size * cap,), torch.int32, x)
+    send_x = _empty((ep_size * cap, H), x.dtype, x)
+    send_ids = _empty((ep_size * cap, K), torch.int32, x)
+    send_w = _empty((ep_size * cap, K), torch.float32, x)
+    need = a2a_dispatch_workspace_size(T, ep_size, cap)
+    if ws is None:
+        ws = _empty((max(need, 1),), torch.uint8, x)
+    _check(lib().moe_a2a_dispatch(_ptr(x), _DT[x.dtype], T, H, K, _ptr(topk_ids), _ptr(topk_w),
+                                  E_global, ep_size, cap, _ptr(offsets), _ptr(token_pos),
+                                  _ptr(send_token), _ptr(send_x), _ptr(send_ids), _ptr(send_w),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream()),
+           "moe_a2a_dispatch")
+    return offsets, token_pos, send_token, send_x, send_ids, send_w
+
+
+def a2a_combine(partial: torch.Tensor, token_pos: torch.Tensor,
+                out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """moe_a2a_combine: out[t] = sum over ranks r (ascending) with
+    token_pos[t, r] >= 0 of partial[token_pos[t, r]]."""
+    _dev(partial, "partial", (torch.float32, torch.bfloat16))
+    _dev(token_pos, "token_pos", torch.int32)
+    T, ep_size = token_pos.shape
+    H = partial.shape[1]
+    out = _empty((T, H), out_dtype or partial.dtype, partial)
+    _check(lib().moe_a2a_combine(_ptr(partial), _DT[partial.dtype], _ptr(token_pos), T, ep_size,
+                                 H, _ptr(out), _DT[out.dtype], _stream()), "moe_a2a_combine")
     return out

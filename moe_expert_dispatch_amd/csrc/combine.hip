@@ -5,7 +5,8 @@
 // reduction of the layer) and TensorRT-LLM PR #10985 review of torch_moe.py
 // (_template_moe applies the routing weights on the output side).
 //
-// Token-major: one block per token reads the token's K (row, weight) pairs,
+// Token-major: one block per token reads the token's K (row, weight) pairs
+// (weight 1 for every pair when no weights are given),
 // gathers the included expert-output rows with 16-byte loads, accumulates in
 // f32 in ascending k with fused multiply-adds and writes the token's output
 // row once. Every output element is written by exactly one thread, so the
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
   __shared__ float wts[MOE_MAX_TOPK];
   if (threadIdx.x < K) {
     rows[threadIdx.x] = pair_row[(size_t)t * K + threadIdx.x];
-    wts[threadIdx.x] = w_masked[(size_t)t * K + threadIdx.x];
+    wts[threadIdx.x] = w_masked != nullptr ? w_masked[(size_t)t * K + threadIdx.x] : 1.0f;
   }
   __syncthreads();
   const int nvec = H / 8;

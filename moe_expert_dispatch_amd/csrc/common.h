@@ -80,10 +80,12 @@ struct PermutePlan {
   size_t ws_bytes;
 };
 PermutePlan permute_plan(int T, int K, int S);
+// seg_cap > 0 places slot s's rows in the fixed block [s * seg_cap,
+// (s + 1) * seg_cap) (the caller guarantees every slot fits).
 moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
                             const int32_t* slot, const uint8_t* mask, int S, int32_t* offsets,
                             int32_t* sorted_pairs, int32_t* pair_row, void* x_perm, void* ws,
-                            hipStream_t stream);
+                            hipStream_t stream, int seg_cap = 0);
 
 moe_status_t launch_gemm_bf16(moe_gemm_op_t op, const void* a, const int32_t* offsets, int S,
                               int max_rows, const void* w, int H, int I, void* c,
@@ -101,6 +103,18 @@ moe_status_t launch_gemm_f32(moe_gemm_op_t op, const void* a, const int32_t* off
                              int max_rows, const void* w, int H, int I, void* c,
                              hipStream_t stream);
 
+// All-to-all dispatch workspace (carved in this order, 256-byte aligned).
+struct A2aLayout {
+  size_t pslot, pmask, psorted, perm_ws, total;
+};
+A2aLayout a2a_layout(int T, int R, int cap);
+moe_status_t launch_a2a_dispatch(const void* x, int elem_bytes, int T, int H, int K,
+                                 const int32_t* ids, const float* w, int E_global, int R, int cap,
+                                 int32_t* offsets, int32_t* token_pos, int32_t* send_token,
+                                 void* send_x, int32_t* send_ids, float* send_w, void* ws,
+                                 hipStream_t stream);
+
+// w_masked may be null: every pair then has weight 1.
 moe_status_t launch_combine(const void* y, moe_dtype_t y_dt, const int32_t* pair_row,
                             const float* w_masked, int T, int K, int H, void* out,
                             moe_dtype_t out_dt, int accumulate, hipStream_t stream);

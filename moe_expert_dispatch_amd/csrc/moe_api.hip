@@ -145,6 +145,26 @@ ForwardLayout forward_layout(const moe_config_t* c) {
   return L;
 }
 
+moe_status_t check_a2a_dispatch(const void* x, moe_dtype_t dt, int T, int H, int K,
+                                const int32_t* ids, const float* w, int E_global, int ep_size,
+                                int cap, const int32_t* offsets, const int32_t* token_pos,
+                                const int32_t* send_token, const void* send_x,
+                                const int32_t* send_ids, const float* send_w) {
+  if (T < 0 || K < 1 || E_global < 1 || ep_size < 1 || cap < T) return MOE_ERR_INVALID_ARG;
+  if (E_global % ep_size != 0) return MOE_ERR_INVALID_ARG;
+  if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+  if (ep_size > MOE_MAX_A2A_RANKS || K > MOE_MAX_TOPK || E_global > MOE_MAX_EXPERTS)
+    return MOE_ERR_UNSUPPORTED;
+  if (H < 1 || (H * dtype_bytes(dt)) % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!pairs_fit(T, ep_size) || !pairs_fit(cap, ep_size) || !pairs_fit(cap * ep_size, K))
+    return MOE_ERR_UNSUPPORTED;
+  if (!offsets) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !ids || !w || !token_pos || !aligned16(x))) return MOE_ERR_INVALID_ARG;
+  if (cap > 0 && (!send_token || !send_x || !send_ids || !send_w || !aligned16(send_x)))
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
 moe_status_t check_config(const moe_config_t* c) {
   if (!c) return MOE_ERR_INVALID_ARG;
   if (c->T_max < 0 || c->T < 0 || c->T > c->T_max) return MOE_ERR_INVALID_ARG;
@@ -316,6 +336,42 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_forward_args_t* args
   MOE_TRY(mark(MOE_EV_COMBINED));
 #undef MOE_TRY
   return MOE_OK;
+}
+
+size_t moe_a2a_dispatch_workspace_size(int T, int ep_size, int cap) {
+  if (T < 0 || ep_size < 1 || ep_size > MOE_MAX_A2A_RANKS || cap < T ||
+      !pairs_fit(T, ep_size) || !pairs_fit(cap, ep_size))
+    return 0;
+  return a2a_layout(T, ep_size, cap).total;
+}
+
+moe_status_t moe_a2a_dispatch(const void* x, moe_dtype_t dt, int T, int H, int K,
+                              const int32_t* topk_ids, const float* topk_w, int E_global,
+                              int ep_size, int cap, int32_t* offsets, int32_t* token_pos,
+                              int32_t* send_token, void* send_x, int32_t* send_ids,
+                              float* send_w, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const moe_status_t st =
+      check_a2a_dispatch(x, dt, T, H, K, topk_ids, topk_w, E_global, ep_size, cap, offsets,
+                         token_pos, send_token, send_x, send_ids, send_w);
+  if (st != MOE_OK) return st;
+  if (!ws || ws_bytes < a2a_layout(T, ep_size, cap).total) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_INVALID_ARG;
+  return launch_a2a_dispatch(x, dtype_bytes(dt), T, H, K, topk_ids, topk_w, E_global, ep_size,
+                             cap, offsets, token_pos, send_token, send_x, send_ids, send_w, ws,
+                             stream);
+}
+
+moe_status_t moe_a2a_combine(const void* partial, moe_dtype_t partial_dt,
+                             const int32_t* token_pos, int T, int ep_size, int H, void* out,
+                             moe_dtype_t out_dt, hipStream_t stream) {
+  if (T < 0 || ep_size < 1) return MOE_ERR_INVALID_ARG;
+  if (!dtype_ok(partial_dt) || !dtype_ok(out_dt)) return MOE_ERR_UNSUPPORTED;
+  if (ep_size > MOE_MAX_A2A_RANKS || H % 8 != 0 || !pairs_fit(T, ep_size))
+    return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && (!partial || !token_pos || !out)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned16(partial) || !aligned16(out))) return MOE_ERR_INVALID_ARG;
+  return launch_combine(partial, partial_dt, token_pos, nullptr, T, ep_size, H, out, out_dt, 0,
+                        stream);
 }
 
 }  // extern "C"

@@ -127,10 +127,14 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict_
 // lanes holding the same slot are ranked with a ballot (lane order = pair
 // order); per-batch slot counts, scanned over the batches, give each batch's
 // base row, so the order inside a slot is the pair order.
+// seg_cap > 0: slot s's rows start at s * seg_cap instead of offsets[s]
+// (fixed-capacity blocks, one per slot).
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ slot,
                                                       const uint8_t* __restrict__ mask, int P,
                                                       int S, int chunk, int nchunks,
                                                       const int32_t* __restrict__ base,
+                                                      const int32_t* __restrict__ offsets,
+                                                      int seg_cap,
                                                       int32_t* __restrict__ sorted_pairs,
                                                       int32_t* __restrict__ pair_row) {
   extern __shared__ int32_t lds[];
@@ -185,7 +189,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
       const int b = wave * kPer + m;
       const int p = q0 + b * kWave + lane;
       if (p < p1) {
-        const int row = inc[m] ? bcount[b * S + s[m]] + rank[m] : -1;
+        int row = inc[m] ? bcount[b * S + s[m]] + rank[m] : -1;
+        if (seg_cap > 0 && row >= 0) row += s[m] * seg_cap - offsets[s[m]];
         pair_row[p] = row;
         if (row >= 0) sorted_pairs[row] = p;
       }
@@ -232,7 +237,7 @@ PermutePlan permute_plan(int T, int K, int S) {
 moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
                             const int32_t* slot, const uint8_t* mask, int S, int32_t* offsets,
                             int32_t* sorted_pairs, int32_t* pair_row, void* x_perm, void* ws,
-                            hipStream_t stream) {
+                            hipStream_t stream, int seg_cap) {
   const PermutePlan pl = permute_plan(T, K, S);
   int32_t* hist = static_cast<int32_t*>(ws);
   const size_t lds = (size_t)S * sizeof(int32_t);
@@ -244,8 +249,8 @@ moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
   if (pl.nchunks > 0) {
     const size_t lds_scatter = (size_t)(1 + kBatches) * S * sizeof(int32_t);
     scatter_kernel<<<pl.nchunks, 256, lds_scatter, stream>>>(slot, mask, pl.P, S, pl.chunk,
-                                                            pl.nchunks, hist, sorted_pairs,
-                                                            pair_row);
+                                                            pl.nchunks, hist, offsets, seg_cap,
+                                                            sorted_pairs, pair_row);
   }
   if (x_perm != nullptr && T > 0) {
     const int nvec = H * elem_bytes / 16;

@@ -21,7 +21,7 @@ INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
 def declared_symbols():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -100,6 +100,37 @@ def test_combine_validation(so):
     assert f(fake, 1, fake, fake, 4, 2, 60, fake, 1, 0, None) == UNSUPPORTED  # H % 8
     assert f(None, 1, fake, fake, 4, 2, 64, fake, 1, 0, None) == INVALID
     assert f(fake, 1, fake, fake, 4, 2, 64, ctypes.c_void_p(260), 1, 0, None) == INVALID
+
+
+def test_a2a_validation_and_workspace(so):
+    ws = moe.a2a_dispatch_workspace_size
+    assert ws(64, 4, 64) > 0
+    assert ws(0, 2, 0) > 0            # empty batch still has a layout
+    assert ws(64, 4, 32) == 0         # cap < T
+    assert ws(64, 0, 64) == 0
+    assert ws(64, 33, 64) == 0        # more ranks than supported
+    f = so.moe_a2a_dispatch
+    fake = ctypes.c_void_p(256)
+    big = ctypes.c_size_t(1 << 30)
+
+    def call(x=fake, dt=1, T=8, H=64, K=2, E=8, ep=2, cap=8, send_x=fake, wsz=big):
+        return f(x, dt, T, H, K, fake, fake, E, ep, cap, fake, fake, fake, send_x, fake, fake,
+                 fake, wsz, None)
+    assert call(cap=4) == INVALID                      # block could overflow
+    assert call(E=9) == INVALID                        # E % ep_size
+    assert call(ep=0) == INVALID
+    assert call(ep=64, E=64) == UNSUPPORTED
+    assert call(K=33, E=64) == UNSUPPORTED
+    assert call(H=4) == UNSUPPORTED                    # 8-byte rows
+    assert call(dt=7) == UNSUPPORTED
+    assert call(x=None) == INVALID
+    assert call(send_x=ctypes.c_void_p(264)) == INVALID  # misaligned
+    assert call(wsz=ctypes.c_size_t(16)) == WORKSPACE
+    g = so.moe_a2a_combine
+    assert g(fake, 1, fake, 8, 0, 64, fake, 1, None) == INVALID
+    assert g(fake, 1, fake, 8, 2, 60, fake, 1, None) == UNSUPPORTED
+    assert g(fake, 1, fake, 8, 33, 64, fake, 1, None) == UNSUPPORTED
+    assert g(None, 1, fake, 8, 2, 64, fake, 1, None) == INVALID
 
 
 def _cfg(**kw):
