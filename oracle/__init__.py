@@ -15,6 +15,7 @@ from .moe_oracle import (  # noqa: F401
     permute_indices,
     permute_rows,
     route,
+    route_grouped,
     silu,
     slot_map,
     softmax,

@@ -103,6 +103,35 @@ def route(logits, K: int, renormalize: bool) -> Tuple[np.ndarray, np.ndarray]:
 # asserted); [SLOTS] Description (expert id -> expert slot; the identity map
 # when every expert has one slot). Replica choice t mod r is a reading.
 # --------------------------------------------------------------------------
+def route_grouped(logits, K: int, renormalize: bool, num_groups: int,
+                  topk_groups: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Group-limited routing ([EPMASK] FusedMoE constructor: use_grouped_topk,
+    num_expert_group, topk_group; the pages name the options only). Reading:
+    the E experts form num_groups consecutive groups; a group's score is the
+    largest softmax probability among its experts (equivalently its largest
+    logit); the topk_groups best groups are kept (score descending, group
+    index ascending on ties) and the top-K experts are chosen among their
+    experts only, with the same key as route(); the weights are the full
+    softmax probabilities, renormalised over the K when renormalize is set."""
+    l = _f64(logits)
+    T, E = l.shape
+    Eg = E // num_groups
+    p = softmax(l)
+    gmax = l.reshape(T, num_groups, Eg).max(axis=2)
+    ids = np.empty((T, K), dtype=np.int64)
+    for t in range(T):
+        order = np.lexsort((np.arange(num_groups), -gmax[t]))[:topk_groups]
+        keep = np.zeros(E, dtype=bool)
+        for g in order:
+            keep[g * Eg:(g + 1) * Eg] = True
+        masked = np.where(keep, l[t], -np.inf)
+        ids[t] = topk_ids(masked[None, :], K)[0]
+    w = np.take_along_axis(p, ids, axis=1)
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    return ids.astype(np.int32), w
+
+
 def ep_partition(E_global: int, ep_size: int, ep_rank: int) -> Tuple[int, int]:
     if ep_size < 1 or E_global % ep_size != 0:
         raise ValueError("E_global must be divisible by ep_size")

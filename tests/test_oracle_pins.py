@@ -118,6 +118,79 @@ def test_route_weights_closed_forms():
     np.testing.assert_allclose(w_all.sum(1), 1.0, atol=1e-14)
 
 
+def test_route_grouped_golden_vectors():
+    for c in load_golden("route_grouped.json")["cases"]:
+        logits = np.array([c["logits"]], dtype=np.float32)
+        ids, w = oracle.route_grouped(logits, c["K"], False, c["num_groups"], c["topk_groups"])
+        assert ids[0].tolist() == c["ids"], c["name"]
+        p = oracle.softmax(logits)[0]
+        np.testing.assert_array_equal(w[0], p[ids[0]])
+
+
+def _grouped_bruteforce(l, K, G, TG):
+    E = len(l)
+    Eg = E // G
+    groups = []
+    for g in range(G):
+        best = max(l[g * Eg:(g + 1) * Eg])
+        groups.append((-best, g))
+    groups.sort()
+    cand = []
+    for _, g in groups[:TG]:
+        for e in range(g * Eg, (g + 1) * Eg):
+            cand.append((-l[e], e))
+    cand.sort()
+    return [e for _, e in cand[:K]]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_route_grouped_bruteforce(seed):
+    rng = np.random.default_rng(200 + seed)
+    E, G, TG, K = [(16, 4, 2, 3), (160, 8, 3, 6), (64, 8, 4, 8), (12, 3, 1, 4), (32, 32, 5, 5),
+                   (8, 2, 2, 8)][seed]
+    T = 20
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    if seed % 2:
+        l = np.round(l * 2) / 2  # many ties
+    ids, w = oracle.route_grouped(l, K, True, G, TG)
+    for t in range(T):
+        assert ids[t].tolist() == _grouped_bruteforce(l[t].tolist(), K, G, TG)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-12)
+
+
+@pytest.mark.parametrize("G,TG", [(1, 1), (4, 4), (8, 8)])
+def test_route_grouped_reduces_to_plain_topk(G, TG):
+    """One group, or every group kept: the grouping selects nothing away."""
+    rng = np.random.default_rng(G)
+    l = rng.standard_normal((30, 32)).astype(np.float32)
+    for renorm in (False, True):
+        a = oracle.route_grouped(l, 5, renorm, G, TG)
+        b = oracle.route(l, 5, renorm)
+        assert np.array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_mutation_grouped_sum_score_is_caught(monkeypatch):
+    # planted mistake: a group scored by the sum of its logits instead of the max
+    def bad(logits, K, renormalize, num_groups, topk_groups):
+        l = np.asarray(logits, dtype=np.float64)
+        T, E = l.shape
+        Eg = E // num_groups
+        gs = l.reshape(T, num_groups, Eg).sum(axis=2)
+        ids = np.empty((T, K), dtype=np.int64)
+        for t in range(T):
+            order = np.lexsort((np.arange(num_groups), -gs[t]))[:topk_groups]
+            keep = np.zeros(E, dtype=bool)
+            for g in order:
+                keep[g * Eg:(g + 1) * Eg] = True
+            ids[t] = om.topk_ids(np.where(keep, l[t], -np.inf)[None, :], K)[0]
+        return ids.astype(np.int32), np.take_along_axis(om.softmax(l), ids, axis=1)
+    monkeypatch.setattr(om, "route_grouped", bad)
+    monkeypatch.setattr(oracle, "route_grouped", bad)
+    with pytest.raises(AssertionError):
+        test_route_grouped_golden_vectors()
+
+
 def test_route_all_equal_logits():
     lg = np.full((3, 7), 0.25, dtype=np.float32)
     ids, w = oracle.route(lg, 3, False)
