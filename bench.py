@@ -166,8 +166,14 @@ def cpu_baseline(inp, seconds, rank=0):
     t0 = time.perf_counter()
     while True:
         tok = np.arange(done, min(done + block, cfg.T))
-        oracle.forward(inp.x, inp.logits, inp.w_gate_up, inp.w_down, cfg.K, cfg.renormalize,
-                       cfg.ep_size, rank, tokens=tok)
+        if cfg.num_expert_group:
+            ids, w = oracle.route_grouped(inp.logits.numpy()[tok], cfg.K, cfg.renormalize,
+                                          cfg.num_expert_group, cfg.topk_group)
+            oracle.forward(inp.x[tok], None, inp.w_gate_up, inp.w_down, cfg.K, False,
+                           cfg.ep_size, rank, topk=(ids, w))
+        else:
+            oracle.forward(inp.x, inp.logits, inp.w_gate_up, inp.w_down, cfg.K,
+                           cfg.renormalize, cfg.ep_size, rank, tokens=tok)
         done += tok.size
         el = time.perf_counter() - t0
         if el >= seconds or done >= cfg.T:
@@ -225,12 +231,14 @@ def main():
 
     fc = moe.ForwardConfig(T=cfg.T, H=cfg.H, I=cfg.I, E_global=cfg.E, K=cfg.K,
                            renormalize=cfg.renormalize, S=S, dtype=tdt, ep_size=cfg.ep_size,
-                           ep_rank=rank)
+                           ep_rank=rank, num_expert_group=cfg.num_expert_group,
+                           topk_group=cfg.topk_group)
     ws = torch.empty(moe.forward_workspace_size(fc), dtype=torch.uint8, device=dev)
     out = torch.empty(cfg.T, cfg.H, dtype=tdt, device=dev)
 
     # included pairs of this batch (all pairs when ep_size == 1)
-    ids, w = moe.route(logits, cfg.K, cfg.renormalize)
+    ids, w = moe.route(logits, cfg.K, cfg.renormalize, num_groups=cfg.num_expert_group,
+                       topk_groups=cfg.topk_group)
     slot, wm, mask = moe.slot_map(ids, w, cfg.E, cfg.ep_size, rank, ro, rs)
     P_in = int(mask.sum().item())
 

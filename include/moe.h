@@ -84,6 +84,7 @@ typedef enum {
 #define MOE_MAX_TOPK 32      /* K */
 #define MOE_MAX_SLOTS 1024   /* S */
 #define MOE_MAX_A2A_RANKS 32 /* ep_size of the all-to-all dispatch */
+#define MOE_MAX_EXPERT_GROUPS 64 /* num_expert_group of group-limited routing */
 
 /* Human-readable name of a status code (static storage). */
 const char* moe_status_str(moe_status_t status);
@@ -108,6 +109,26 @@ const char* moe_status_str(moe_status_t status);
  */
 moe_status_t moe_route(const float* logits, int T, int E, int K, int renormalize,
                        int32_t* ids, float* w, hipStream_t stream);
+
+/*
+ * moe_route_grouped -- group-limited routing.
+ *   Source: [EPMASK] FusedMoE constructor arguments use_grouped_topk,
+ *   num_expert_group and topk_group (the pages name them; the selection
+ *   below is the plainest reading).
+ *
+ * As moe_route, except that the K experts are chosen among the experts of
+ * the topk_groups best groups: the E experts form num_groups consecutive
+ * groups of E / num_groups; a group's score is its largest logit (equivalently
+ * its largest probability); groups are ranked by score descending, lower
+ * group index first on ties. Weights are the probabilities of the full
+ * softmax over all E experts (renormalised over the K when renormalize != 0).
+ * Limits: 1 <= topk_groups <= num_groups <= MOE_MAX_EXPERT_GROUPS,
+ * E % num_groups == 0, K <= topk_groups * (E / num_groups)
+ * (MOE_ERR_INVALID_ARG otherwise; more groups: MOE_ERR_UNSUPPORTED).
+ */
+moe_status_t moe_route_grouped(const float* logits, int T, int E, int K, int renormalize,
+                               int num_groups, int topk_groups, int32_t* ids, float* w,
+                               hipStream_t stream);
 
 /*
  * moe_slot_map -- expert-parallel mask / remap and expert -> slot lookup.
@@ -220,6 +241,8 @@ typedef struct {
   moe_dtype_t dtype;     /* x, weights and intermediates */
   moe_dtype_t out_dtype; /* out */
   int accumulate;   /* add into out instead of overwriting it */
+  int num_expert_group; /* 0: plain top-K; else group-limited routing (moe_route_grouped) */
+  int topk_group;       /* groups kept when num_expert_group > 0 */
 } moe_config_t;
 
 /* Stage boundaries at which moe_forward records the caller's events. */
@@ -253,6 +276,8 @@ typedef struct {
  *
  * moe_forward -- route (or take topk_ids / topk_w), slot map, permute,
  * grouped GEMM 1, grouped GEMM 2 and combine, all enqueued on `stream`.
+ * Routing from logits is moe_route, or moe_route_grouped when
+ * cfg->num_expert_group > 0 (cfg->topk_group groups kept).
  * Equivalent to calling the staged entry points in that order. Intermediate
  * activations are stored in cfg->dtype. The workspace layout is internal;
  * its contents on entry are ignored.

@@ -49,7 +49,8 @@ _sz = ctypes.c_size_t
 class _Config(ctypes.Structure):
     _fields_ = [("T_max", _i), ("T", _i), ("H", _i), ("I", _i), ("E_global", _i), ("K", _i),
                 ("renormalize", _i), ("ep_size", _i), ("ep_rank", _i), ("S", _i),
-                ("dtype", _i), ("out_dtype", _i), ("accumulate", _i)]
+                ("dtype", _i), ("out_dtype", _i), ("accumulate", _i),
+                ("num_expert_group", _i), ("topk_group", _i)]
 
 
 class _ForwardArgs(ctypes.Structure):
@@ -61,6 +62,7 @@ class _ForwardArgs(ctypes.Structure):
 _SIGS = {
     "moe_status_str": (ctypes.c_char_p, [_i]),
     "moe_route": (_i, [_p, _i, _i, _i, _i, _p, _p, _p]),
+    "moe_route_grouped": (_i, [_p, _i, _i, _i, _i, _i, _i, _p, _p, _p]),
     "moe_slot_map": (_i, [_p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p]),
     "moe_permute_workspace_size": (_sz, [_i, _i, _i]),
     "moe_permute": (_i, [_p, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p]),
@@ -138,17 +140,23 @@ def _empty(shape, dtype, like: torch.Tensor) -> torch.Tensor:
 
 # ---------------------------------------------------------------- stages
 def route(logits: torch.Tensor, K: int, renormalize: bool,
-          ids: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None
-          ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """moe_route: logits [T, E] f32 -> (ids [T, K] int32, w [T, K] f32)."""
+          ids: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
+          num_groups: int = 0, topk_groups: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """moe_route (or moe_route_grouped when num_groups > 0):
+    logits [T, E] f32 -> (ids [T, K] int32, w [T, K] f32)."""
     _dev(logits, "logits", torch.float32)
     if logits.dim() != 2:
         raise ValueError("logits must be [T, E]")
     T, E = logits.shape
     ids = _empty((T, K), torch.int32, logits) if ids is None else _dev(ids, "ids", torch.int32, (T, K))
     w = _empty((T, K), torch.float32, logits) if w is None else _dev(w, "w", torch.float32, (T, K))
-    _check(lib().moe_route(_ptr(logits), T, E, K, int(bool(renormalize)), _ptr(ids), _ptr(w),
-                           _stream()), "moe_route")
+    if num_groups:
+        _check(lib().moe_route_grouped(_ptr(logits), T, E, K, int(bool(renormalize)), num_groups,
+                                       topk_groups, _ptr(ids), _ptr(w), _stream()),
+               "moe_route_grouped")
+    else:
+        _check(lib().moe_route(_ptr(logits), T, E, K, int(bool(renormalize)), _ptr(ids),
+                               _ptr(w), _stream()), "moe_route")
     return ids, w
 
 
@@ -270,17 +278,19 @@ class ForwardConfig:
     def __init__(self, T: int, H: int, I: int, E_global: int, K: int, renormalize: bool,
                  S: int, dtype: torch.dtype, out_dtype: Optional[torch.dtype] = None,
                  ep_size: int = 1, ep_rank: int = 0, accumulate: bool = False,
-                 T_max: Optional[int] = None):
+                 T_max: Optional[int] = None, num_expert_group: int = 0, topk_group: int = 0):
         self.T, self.H, self.I, self.E_global, self.K = T, H, I, E_global, K
         self.renormalize, self.S, self.dtype = bool(renormalize), S, dtype
         self.out_dtype = out_dtype or dtype
         self.ep_size, self.ep_rank, self.accumulate = ep_size, ep_rank, bool(accumulate)
         self.T_max = T if T_max is None else T_max
+        self.num_expert_group, self.topk_group = num_expert_group, topk_group
 
     def c_struct(self) -> _Config:
         return _Config(self.T_max, self.T, self.H, self.I, self.E_global, self.K,
                        int(self.renormalize), self.ep_size, self.ep_rank, self.S,
-                       _DT[self.dtype], _DT[self.out_dtype], int(self.accumulate))
+                       _DT[self.dtype], _DT[self.out_dtype], int(self.accumulate),
+                       self.num_expert_group, self.topk_group)
 
 
 def forward_workspace_size(cfg: ForwardConfig) -> int:

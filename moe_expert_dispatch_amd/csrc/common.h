@@ -66,8 +66,9 @@ int device_cu_count();
 
 // ---------------------------------------------------------------- launchers
 // Host-side launchers; arguments are validated by the C-ABI layer.
-moe_status_t launch_route(const float* logits, int T, int E, int K, int renorm, int32_t* ids,
-                          float* w, hipStream_t stream);
+// G == 0: plain top-K; else group-limited routing over G groups keeping TG.
+moe_status_t launch_route(const float* logits, int T, int E, int K, int renorm, int G, int TG,
+                          int32_t* ids, float* w, hipStream_t stream);
 moe_status_t launch_slot_map(const int32_t* ids, const float* w, int T, int K, int start,
                              int E_local, const int32_t* rep_off, const int32_t* rep_slots,
                              int S, int32_t* slot, float* w_masked, uint8_t* mask,

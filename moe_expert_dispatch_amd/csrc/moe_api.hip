@@ -165,6 +165,15 @@ moe_status_t check_a2a_dispatch(const void* x, moe_dtype_t dt, int T, int H, int
   return MOE_OK;
 }
 
+// Group-limited routing: 1 <= topk_groups <= num_groups <= 64, E divisible
+// by num_groups, and the kept groups hold at least K experts.
+moe_status_t check_groups(int E, int K, int num_groups, int topk_groups) {
+  if (num_groups < 1 || topk_groups < 1 || topk_groups > num_groups) return MOE_ERR_INVALID_ARG;
+  if (E % num_groups != 0 || K > topk_groups * (E / num_groups)) return MOE_ERR_INVALID_ARG;
+  if (num_groups > MOE_MAX_EXPERT_GROUPS) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 moe_status_t check_config(const moe_config_t* c) {
   if (!c) return MOE_ERR_INVALID_ARG;
   if (c->T_max < 0 || c->T < 0 || c->T > c->T_max) return MOE_ERR_INVALID_ARG;
@@ -180,6 +189,10 @@ moe_status_t check_config(const moe_config_t* c) {
   if (c->H % 8 != 0 || c->I % 8 != 0 || !pairs_fit(c->T_max, c->K)) return MOE_ERR_UNSUPPORTED;
   const long long P = (long long)c->T_max * c->K;
   if (P * (c->H > c->I ? c->H : c->I) >= (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  if (c->num_expert_group != 0 || c->topk_group != 0) {
+    const moe_status_t sg = check_groups(c->E_global, c->K, c->num_expert_group, c->topk_group);
+    if (sg != MOE_OK) return sg;
+  }
   return MOE_OK;
 }
 
@@ -205,7 +218,18 @@ moe_status_t moe_route(const float* logits, int T, int E, int K, int renormalize
                        float* w, hipStream_t stream) {
   const moe_status_t st = check_route(logits, T, E, K, ids, w);
   if (st != MOE_OK) return st;
-  return launch_route(logits, T, E, K, renormalize ? 1 : 0, ids, w, stream);
+  return launch_route(logits, T, E, K, renormalize ? 1 : 0, 0, 0, ids, w, stream);
+}
+
+moe_status_t moe_route_grouped(const float* logits, int T, int E, int K, int renormalize,
+                               int num_groups, int topk_groups, int32_t* ids, float* w,
+                               hipStream_t stream) {
+  const moe_status_t st = check_route(logits, T, E, K, ids, w);
+  if (st != MOE_OK) return st;
+  const moe_status_t sg = check_groups(E, K, num_groups, topk_groups);
+  if (sg != MOE_OK) return sg;
+  return launch_route(logits, T, E, K, renormalize ? 1 : 0, num_groups, topk_groups, ids, w,
+                      stream);
 }
 
 moe_status_t moe_slot_map(const int32_t* ids, const float* w, int T, int K, int E_global,
@@ -306,8 +330,8 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_forward_args_t* args
   const int32_t* ids_in = args->topk_ids;
   const float* w_in = args->topk_w;
   if (args->logits) {
-    MOE_TRY(launch_route(args->logits, T, cfg->E_global, K, cfg->renormalize ? 1 : 0, ids, w,
-                         stream));
+    MOE_TRY(launch_route(args->logits, T, cfg->E_global, K, cfg->renormalize ? 1 : 0,
+                         cfg->num_expert_group, cfg->topk_group, ids, w, stream));
     ids_in = ids;
     w_in = w;
   }

@@ -11,6 +11,13 @@
 // high word and (0xffffffff - id) in the low word, so one unsigned max picks
 // the largest logit and, among equal logits, the lowest id. K rounds of a
 // wave-wide max select the experts; the winner's owner lane clears its key.
+//
+// Group-limited routing (the constructor's use_grouped_topk,
+// num_expert_group and topk_group, which the pages only name; reading: the
+// E experts form G consecutive groups scored by their largest logit): lane g
+// gets group g's key (best ordered logit, 0xffffffff - g), topk_group rounds
+// of a wave max pick the groups, and the keys of experts outside them are
+// cleared before the K rounds. The softmax still runs over all E experts.
 #include "common.h"
 
 namespace moe {
@@ -23,9 +30,19 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = __shfl_xor(v, off, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// G == 0: plain top-K over all experts; otherwise 1 <= TG <= G <= 64, E % G == 0.
 template <int EPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T,
-                                                    int E, int K, int renorm,
+                                                    int E, int K, int renorm, int G, int TG,
                                                     int32_t* __restrict__ ids,
                                                     float* __restrict__ w) {
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
@@ -44,6 +61,36 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     } else {
       v[j] = -INFINITY;
       key[j] = 0;  // never selected: every real candidate has a non-zero key
+    }
+  }
+
+  if (G > 0) {
+    const int Eg = E / G;
+    uint64_t gkey = 0;
+    for (int g = 0; g < G; ++g) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = lane + kWave * j;
+        if (e < E && e / Eg == g) {
+          const uint32_t o = (uint32_t)(key[j] >> 32);
+          m = o > m ? o : m;
+        }
+      }
+      m = wave_max_u32(m);
+      if (lane == g) gkey = ((uint64_t)m << 32) | (0xffffffffu - (uint32_t)g);
+    }
+    uint64_t keep = 0;  // selected groups, the same in every lane
+    for (int r = 0; r < TG; ++r) {
+      const uint64_t best = wave_max_u64(gkey);
+      const int g = (int)(0xffffffffu - (uint32_t)best);
+      keep |= 1ull << g;
+      if (lane == g) gkey = 0;
+    }
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + kWave * j;
+      if (e < E && !((keep >> (e / Eg)) & 1ull)) key[j] = 0;
     }
   }
 
@@ -85,22 +132,22 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 
 }  // namespace
 
-moe_status_t launch_route(const float* logits, int T, int E, int K, int renorm, int32_t* ids,
-                          float* w, hipStream_t stream) {
+moe_status_t launch_route(const float* logits, int T, int E, int K, int renorm, int G, int TG,
+                          int32_t* ids, float* w, hipStream_t stream) {
   if (T == 0) return MOE_OK;
   const dim3 block(256);
   const dim3 grid(ceil_div(T, 256 / kWave));
   const int epl = ceil_div(E, kWave);
   if (epl <= 1)
-    route_kernel<1><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, ids, w);
+    route_kernel<1><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, G, TG, ids, w);
   else if (epl <= 2)
-    route_kernel<2><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, ids, w);
+    route_kernel<2><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, G, TG, ids, w);
   else if (epl <= 4)
-    route_kernel<4><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, ids, w);
+    route_kernel<4><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, G, TG, ids, w);
   else if (epl <= 8)
-    route_kernel<8><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, ids, w);
+    route_kernel<8><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, G, TG, ids, w);
   else
-    route_kernel<16><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, ids, w);
+    route_kernel<16><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, G, TG, ids, w);
   return launch_status();
 }
 

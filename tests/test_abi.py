@@ -53,6 +53,21 @@ def test_route_validation(so):
     assert f(None, 4, 64, 33, 1, None, None, None) == UNSUPPORTED   # K > 32
 
 
+def test_route_grouped_validation(so):
+    f = so.moe_route_grouped
+    fake = ctypes.c_void_p(256)
+
+    def call(E=16, K=3, G=4, TG=2, T=4):
+        return f(fake, T, E, K, 1, G, TG, fake, fake, None)
+    assert call(G=0) == INVALID
+    assert call(TG=0) == INVALID
+    assert call(TG=5) == INVALID           # more groups kept than exist
+    assert call(G=3) == INVALID            # 16 % 3
+    assert call(K=9, TG=2) == INVALID      # two groups of 4 hold only 8 experts
+    assert call(E=256, K=4, G=128, TG=2) == UNSUPPORTED
+    assert f(None, 4, 16, 3, 1, 4, 2, None, None, None) == INVALID  # null pointers
+
+
 def test_slot_map_validation(so):
     f = so.moe_slot_map
     # E_global % ep_size != 0 (the divisibility the EP partition asserts)
@@ -146,7 +161,12 @@ def test_forward_workspace_and_validation(so):
     P = 16 * 2
     assert n >= P * (4 * 6 + 1) + P * 64 * 2 * 2  # index arrays + x_perm + activations
     bad = [_cfg(K=9), _cfg(E_global=10, ep_size=4), _cfg(ep_size=2, ep_rank=2, S=4),
-           _cfg(S=3), _cfg(H=60), _cfg(T=32, T_max=16)]
+           _cfg(S=3), _cfg(H=60), _cfg(T=32, T_max=16),
+           _cfg(num_expert_group=3, topk_group=1),      # 8 % 3
+           _cfg(num_expert_group=4, topk_group=0),
+           _cfg(num_expert_group=8, topk_group=1, K=2)]  # one group of 1 expert < K
+    assert so.moe_forward_workspace_size(
+        ctypes.byref(_cfg(num_expert_group=4, topk_group=2).c_struct())) > 0
     for b in bad:
         assert so.moe_forward_workspace_size(ctypes.byref(b.c_struct())) == 0
     # workspace too small is reported before any launch

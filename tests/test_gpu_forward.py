@@ -71,7 +71,8 @@ def run_forward(inp, dev, ep_rank=0, replicas=False, flip=False, out=None, accum
     fc = moe.ForwardConfig(T=cfg.T, H=cfg.H, I=cfg.I, E_global=cfg.E, K=cfg.K,
                            renormalize=cfg.renormalize, S=S, dtype=_TDT[cfg.dtype],
                            out_dtype=out_dtype, ep_size=cfg.ep_size, ep_rank=ep_rank,
-                           accumulate=accumulate, T_max=T_max)
+                           accumulate=accumulate, T_max=T_max,
+                           num_expert_group=cfg.num_expert_group, topk_group=cfg.topk_group)
     kw = dict(rep_off=ro, rep_slots=rs, out=out, ws=ws)
     if topk is None:
         kw["logits"] = inp.logits.to(dev)
@@ -94,11 +95,12 @@ def check_staged_indices(inp, dev, ep_rank=0, replicas=False):
     wgu, wd, ro, rs, S = share_tensors(inp, dev, ep_rank, replicas) if replicas else \
         (None, None, *identity_slot_table(cfg.E_local), cfg.E_local)
     ro, rs = ro.to(dev), rs.to(dev)
-    ids, w = moe.route(inp.logits.to(dev), cfg.K, cfg.renormalize)
+    ids, w = moe.route(inp.logits.to(dev), cfg.K, cfg.renormalize,
+                       num_groups=cfg.num_expert_group, topk_groups=cfg.topk_group)
     slot, wm, mask = moe.slot_map(ids, w, cfg.E, cfg.ep_size, ep_rank, ro, rs)
     off, sp, pr, xp = moe.permute(inp.x.to(dev), slot, mask, S)
     torch.cuda.synchronize()
-    r_ids, _ = oracle.route(inp.logits, cfg.K, cfg.renormalize)
+    r_ids, _ = oracle_route(inp)
     assert np.array_equal(ids.cpu().numpy(), r_ids)
     r_slot, _, r_mask = oracle.slot_map(ids.cpu(), w.cpu().double(), cfg.E, cfg.ep_size, ep_rank,
                                         ro.cpu().numpy(), rs.cpu().numpy())
@@ -116,11 +118,25 @@ def check_staged_indices(inp, dev, ep_rank=0, replicas=False):
                        ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref)
 
 
+def oracle_route(inp):
+    """The oracle's routing of a workload (group-limited when configured)."""
+    cfg = inp.cfg
+    if cfg.num_expert_group:
+        return oracle.route_grouped(inp.logits.numpy(), cfg.K, cfg.renormalize,
+                                    cfg.num_expert_group, cfg.topk_group)
+    return oracle.route(inp.logits, cfg.K, cfg.renormalize)
+
+
 def compare_tokens(got_dev, inp, tokens, ep_rank=0, what=""):
     cfg = inp.cfg
     got = np64(got_dev[torch.from_numpy(tokens).to(got_dev.device)].cpu())
-    ref = oracle.forward(inp.x, inp.logits, inp.w_gate_up, inp.w_down, cfg.K, cfg.renormalize,
-                         cfg.ep_size, ep_rank, tokens=tokens)
+    if cfg.num_expert_group:
+        ids, w = oracle_route(inp)
+        ref = oracle.forward(inp.x, None, inp.w_gate_up, inp.w_down, cfg.K, False, cfg.ep_size,
+                             ep_rank, tokens=tokens, topk=(ids, w))
+    else:
+        ref = oracle.forward(inp.x, inp.logits, inp.w_gate_up, inp.w_down, cfg.K,
+                             cfg.renormalize, cfg.ep_size, ep_rank, tokens=tokens)
     assert_close(got, ref, tol_of(cfg), what)
     return got, ref
 
@@ -137,7 +153,8 @@ def test_forward_tiny_fp32_all_tokens(dev):
     check_staged_indices(inp, dev)
 
 
-@pytest.mark.parametrize("name,n_sample", [("qwen2_moe_bf16", 64), ("deepseek_v2_bf16", 24)])
+@pytest.mark.parametrize("name,n_sample", [("qwen2_moe_bf16", 64), ("deepseek_v2_bf16", 24),
+                                           ("deepseek_v2_grouped_bf16", 24)])
 def test_forward_full_size_sampled(dev, name, n_sample):
     inp = inputs(name)
     cfg = inp.cfg
@@ -353,3 +370,25 @@ def test_forward_zero_tokens(dev):
     out = run_forward(inp, dev, T_max=16)
     torch.cuda.synchronize()
     assert out.shape == (0, cfg.H)
+
+
+def test_forward_grouped_routing(dev):
+    """moe_forward with num_expert_group / topk_group set routes with the
+    group-limited selection: compare with the oracle forward fed by
+    oracle.route_grouped."""
+    cfg = WorkloadConfig("g1", T=300, H=256, I=192, E=16, K=4, renormalize=True, dtype="bf16",
+                         router="gauss_bias", bias_std=0.5, seed=21)
+    inp = make_inputs(cfg)
+    announce("forward grouped routing E=16 G=4 TG=2")
+    fc = moe.ForwardConfig(T=cfg.T, H=cfg.H, I=cfg.I, E_global=cfg.E, K=cfg.K,
+                           renormalize=True, S=cfg.E, dtype=torch.bfloat16,
+                           num_expert_group=4, topk_group=2)
+    got = moe.forward(fc, inp.x.to(dev), inp.w_gate_up.to(dev), inp.w_down.to(dev),
+                      logits=inp.logits.to(dev))
+    torch.cuda.synchronize()
+    ids, w = oracle.route_grouped(inp.logits.numpy(), cfg.K, True, 4, 2)
+    ref = oracle.forward(inp.x, None, inp.w_gate_up, inp.w_down, cfg.K, False, topk=(ids, w))
+    assert_close(np64(got), ref, BF16_TOL, "grouped-routing forward")
+    # the grouping must matter for this input, or the test proves nothing
+    plain, _ = oracle.route(inp.logits.numpy(), cfg.K, True)
+    assert not np.array_equal(plain, ids)

@@ -63,12 +63,16 @@ ROUTE_CASES = list(CONFIGS) + ["ties", "k_eq_e", "max_e_k", "e1", "e65_ragged", 
 def test_route_parity(dev, name):
     logits, K, renorm = _route_case(name)
     logits = logits.float().contiguous()
-    announce(f"route {name} T={logits.shape[0]} E={logits.shape[1]} K={K} renorm={renorm}")
-    ids, w = moe.route(logits.to(dev), K, renorm)
+    G, TG = (CONFIGS[name].num_expert_group, CONFIGS[name].topk_group) if name in CONFIGS \
+        else (0, 0)
+    announce(f"route {name} T={logits.shape[0]} E={logits.shape[1]} K={K} renorm={renorm} "
+             f"groups={G}/{TG}")
+    ids, w = moe.route(logits.to(dev), K, renorm, num_groups=G, topk_groups=TG)
     torch.cuda.synchronize()
     if logits.shape[0] == 0:
         return
-    ref_ids, ref_w = oracle.route(logits, K, renorm)
+    ref_ids, ref_w = (oracle.route_grouped(logits.numpy(), K, renorm, G, TG) if G
+                      else oracle.route(logits, K, renorm))
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
     assert_close(np64(w), ref_w, (1e-5, 1e-9), "route weights")
 
@@ -316,3 +320,30 @@ def test_combine_single_pair_is_exact_copy(dev):
     got = moe.combine(y.to(dev), perm.to(dev), w.to(dev), 1, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(got.cpu().view(torch.int16), y[perm.long()].view(torch.int16))
+
+
+# ------------------------------------------------------------------ grouped routing
+@pytest.mark.parametrize("E,G,TG,K,ties,T", [
+    (160, 8, 3, 6, False, 777),
+    (256, 8, 4, 8, True, 512),
+    (64, 64, 6, 6, False, 300),
+    (16, 1, 1, 4, True, 65),
+    (128, 16, 16, 8, False, 200),
+    (96, 4, 1, 24, True, 130),
+    (32, 4, 2, 3, False, 0),
+])
+def test_route_grouped_parity(dev, E, G, TG, K, ties, T):
+    announce(f"route grouped E={E} G={G} TG={TG} K={K} ties={ties} T={T}")
+    g = torch.Generator().manual_seed(E + G + TG)
+    logits = torch.randn(T, E, generator=g)
+    if ties:
+        logits = torch.round(logits * 2) / 2
+    logits = logits.float().contiguous()
+    for renorm in (False, True):
+        ids, w = moe.route(logits.to(dev), K, renorm, num_groups=G, topk_groups=TG)
+        torch.cuda.synchronize()
+        if T == 0:
+            continue
+        ref_ids, ref_w = oracle.route_grouped(logits.numpy(), K, renorm, G, TG)
+        assert np.array_equal(ids.cpu().numpy(), ref_ids)
+        assert_close(np64(w), ref_w, (1e-5, 1e-9), "grouped route weights")

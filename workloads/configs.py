@@ -39,6 +39,8 @@ class WorkloadConfig:
     bias_std: float = 0.0     # per-expert logit bias std (gauss_bias)
     zipf_s: float = 1.2
     seed: int = 0
+    num_expert_group: int = 0  # group-limited routing: groups (0 = plain top-K)
+    topk_group: int = 0        # groups kept
 
     @property
     def E_local(self) -> int:
@@ -70,6 +72,10 @@ CONFIGS = {
                        renormalize=True, dtype="bf16", router="gauss", ep_size=4),
         WorkloadConfig("redundant_slots_zipf", T=16384, H=4096, I=1024, E=64, K=8,
                        renormalize=True, dtype="bf16", router="zipf", n_replicated=16),
+        # the 160-expert layer routed with 8 groups of 20 experts, 3 groups kept
+        WorkloadConfig("deepseek_v2_grouped_bf16", T=8192, H=5120, I=1536, E=160, K=6,
+                       renormalize=True, dtype="bf16", router="gauss_bias", bias_std=0.5,
+                       num_expert_group=8, topk_group=3),
     ]
 }
 
