@@ -316,7 +316,8 @@ def combine_rows(y, pair_row, w_masked, K: int) -> np.ndarray:
 def forward(x, logits, w_gate_up, w_down, K: int, renormalize: bool,
             ep_size: int = 1, ep_rank: int = 0,
             tokens: Optional[Sequence[int]] = None,
-            topk: Optional[Tuple[np.ndarray, np.ndarray]] = None) -> np.ndarray:
+            topk: Optional[Tuple[np.ndarray, np.ndarray]] = None,
+            routing_on_input: bool = False, shared=None) -> np.ndarray:
     """Output rows for `tokens` (default: all), fp64 [n, H].
 
     x [T, H]; logits [T, E_global]; w_gate_up [E_global, 2I, H] and
@@ -326,6 +327,10 @@ def forward(x, logits, w_gate_up, w_down, K: int, renormalize: bool,
     Each included pair (t, k) with expert e contributes
     w_masked[t,k] * MLP_e(x[t]); the MLP of expert e is evaluated for all of
     its pairs at once with library matmuls (each row independent).
+    routing_on_input ([A2A] review: _template_moe's apply_routing_on_input):
+    the pair contributes MLP_e(w_masked[t,k] * x[t]) instead.
+    shared [T, H] ([EPMASK] ep_reduce_output: out = routed_out + shared_out):
+    added to the routed sum of each returned token.
     """
     T = (logits.shape[0] if topk is None else np.asarray(topk[0]).shape[0])
     tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
@@ -345,9 +350,14 @@ def forward(x, logits, w_gate_up, w_down, K: int, renormalize: bool,
         if sel[0].size == 0:
             continue
         wgu = _f64(w_gate_up[e])
-        y[sel] = swiglu_mlp(xt[sel[0]], wgu[:I], wgu[I:], w_down[e])
+        xin = xt[sel[0]]
+        if routing_on_input:
+            xin = w_masked[sel][:, None] * xin
+        y[sel] = swiglu_mlp(xin, wgu[:I], wgu[I:], w_down[e])
     out = np.zeros((n, xt.shape[1]))
     for k in range(K):
         m = mask[:, k]
-        out[m] += w_masked[m, k, None] * y[m, k]
+        out[m] += (1.0 if routing_on_input else w_masked[m, k, None]) * y[m, k]
+    if shared is not None:
+        out += _f64(_take_rows(shared, tok))
     return out

@@ -31,10 +31,13 @@ def py_topk(row, K):
     return sorted(range(len(row)), key=lambda e: (-float(row[e]), e))[:K]
 
 
-def dense_brute(x, logits, wgu, wd, K, renorm, ep_size=1, ep_rank=0, w_override=None):
+def dense_brute(x, logits, wgu, wd, K, renorm, ep_size=1, ep_rank=0, w_override=None,
+                on_input=False):
     """Dense gating in torch fp64: every local expert on every token,
     out = sum_e G[t,e] * MLP_e(x_t), with G from a pure-Python full sort and
-    torch.softmax; the MLP uses torch's silu and matmul."""
+    torch.softmax; the MLP uses torch's silu and matmul. on_input: out =
+    sum_e MLP_e(G[t,e] * x_t) (an unselected expert has G = 0 and, with no
+    biases, MLP_e(0) = 0)."""
     x = torch.as_tensor(np.asarray(x, dtype=np.float64))
     lg = np.asarray(logits, dtype=np.float64)
     T, E = lg.shape
@@ -57,9 +60,13 @@ def dense_brute(x, logits, wgu, wd, K, renorm, ep_size=1, ep_rank=0, w_override=
     for e in range(lo, hi):
         w = torch.as_tensor(np.asarray(wgu[e], dtype=np.float64))
         d = torch.as_tensor(np.asarray(wd[e], dtype=np.float64))
-        g = x @ w[:I].T
-        u = x @ w[I:].T
-        out += G[:, e:e + 1] * ((F.silu(g) * u) @ d.T)
+        if on_input:
+            xe = G[:, e:e + 1] * x
+            out += (F.silu(xe @ w[:I].T) * (xe @ w[I:].T)) @ d.T
+        else:
+            g = x @ w[:I].T
+            u = x @ w[I:].T
+            out += G[:, e:e + 1] * ((F.silu(g) * u) @ d.T)
     return out.numpy()
 
 
@@ -414,6 +421,58 @@ def dense_error(seed, K=3, renorm=True, ep_size=1, ep_rank=0, ties=False, E=6):
     (6, True, 1, 0, True), (2, True, 2, 1, False), (4, False, 3, 0, True), (3, True, 3, 2, False)])
 def test_forward_matches_dense_bruteforce(seed, K, renorm, ep_size, ep_rank, ties):
     assert dense_error(seed, K, renorm, ep_size, ep_rank, ties) < 1e-12
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("K,renorm,ep_size,ep_rank", [(3, True, 1, 0), (2, False, 1, 0),
+                                                      (4, True, 2, 1), (6, True, 1, 0)])
+def test_routing_on_input_matches_dense_bruteforce(seed, K, renorm, ep_size, ep_rank):
+    x, lg, wgu, wd = tiny_problem(seed, K=K)
+    out = oracle.forward(x, lg, wgu, wd, K, renorm, ep_size, ep_rank, routing_on_input=True)
+    ref = dense_brute(x, lg, wgu, wd, K, renorm, ep_size, ep_rank, on_input=True)
+    assert np.abs(out - ref).max() < 1e-12
+    # SwiGLU is not linear, so the two placements of the weight differ
+    other = oracle.forward(x, lg, wgu, wd, K, renorm, ep_size, ep_rank)
+    assert np.abs(out - other).max() > 1e-3
+
+
+def test_routing_on_input_with_unit_weight_is_output_side():
+    """K = 1 with renormalisation gives every pair weight 1: MLP(1 * x) = 1 * MLP(x)."""
+    x, lg, wgu, wd = tiny_problem(9, K=1)
+    a = oracle.forward(x, lg, wgu, wd, 1, True, routing_on_input=True)
+    b = oracle.forward(x, lg, wgu, wd, 1, True)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_shared_output_is_added():
+    x, lg, wgu, wd = tiny_problem(10)
+    sh = np.random.default_rng(1).standard_normal(x.shape)
+    for on_input in (False, True):
+        a = oracle.forward(x, lg, wgu, wd, 3, True, routing_on_input=on_input, shared=sh)
+        b = oracle.forward(x, lg, wgu, wd, 3, True, routing_on_input=on_input)
+        np.testing.assert_allclose(a - b, sh, rtol=0, atol=1e-12)
+    tok = np.array([4, 0, 7])
+    a = oracle.forward(x, lg, wgu, wd, 3, True, tokens=tok, shared=sh)
+    b = oracle.forward(x, lg, wgu, wd, 3, True, tokens=tok)
+    np.testing.assert_allclose(a - b, sh[tok], rtol=0, atol=1e-12)
+
+
+def test_mutation_unscaled_input_is_caught(monkeypatch):
+    real = om.forward
+
+    def bad(x, logits, wgu, wd, K, renorm, ep_size=1, ep_rank=0, tokens=None, topk=None,
+            routing_on_input=False, shared=None):
+        if not routing_on_input:
+            return real(x, logits, wgu, wd, K, renorm, ep_size, ep_rank, tokens, topk,
+                        shared=shared)
+        # planted mistake: the experts see x itself, combined with unit weights
+        ids, w = om.route(logits, K, renorm)
+        return real(x, None, wgu, wd, K, False, ep_size, ep_rank, tokens,
+                    topk=(ids, np.ones_like(w)), shared=shared)
+    monkeypatch.setattr(om, "forward", bad)
+    monkeypatch.setattr(oracle, "forward", bad)
+    with pytest.raises(AssertionError):
+        test_routing_on_input_matches_dense_bruteforce(0, 3, False, 1, 0)
 
 
 def test_zero_weight_pairs_contribute_nothing():
