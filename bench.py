@@ -173,7 +173,9 @@ def cpu_baseline(inp, seconds, rank=0):
                            cfg.ep_size, rank, topk=(ids, w))
         else:
             oracle.forward(inp.x, inp.logits, inp.w_gate_up, inp.w_down, cfg.K,
-                           cfg.renormalize, cfg.ep_size, rank, tokens=tok)
+                           cfg.renormalize, cfg.ep_size, rank, tokens=tok,
+                           routing_on_input=cfg.routing_on_input,
+                           shared=np.zeros((cfg.T, cfg.H)) if cfg.shared_expert else None)
         done += tok.size
         el = time.perf_counter() - t0
         if el >= seconds or done >= cfg.T:
@@ -232,7 +234,11 @@ def main():
     fc = moe.ForwardConfig(T=cfg.T, H=cfg.H, I=cfg.I, E_global=cfg.E, K=cfg.K,
                            renormalize=cfg.renormalize, S=S, dtype=tdt, ep_size=cfg.ep_size,
                            ep_rank=rank, num_expert_group=cfg.num_expert_group,
-                           topk_group=cfg.topk_group)
+                           topk_group=cfg.topk_group, routing_on_input=cfg.routing_on_input)
+    shared = None
+    if cfg.shared_expert:  # stands for the shared expert's output (not computed here)
+        shared = torch.randn(cfg.T, cfg.H, generator=torch.Generator().manual_seed(1)).to(
+            tdt).to(dev)
     ws = torch.empty(moe.forward_workspace_size(fc), dtype=torch.uint8, device=dev)
     out = torch.empty(cfg.T, cfg.H, dtype=tdt, device=dev)
 
@@ -244,7 +250,7 @@ def main():
 
     def step(events=None):
         moe.forward(fc, x, wgu, wd, logits=logits, rep_off=ro, rep_slots=rs, out=out, ws=ws,
-                    events=events)
+                    events=events, shared_out=shared)
 
     for _ in range(args.warmup):
         step()
@@ -282,11 +288,13 @@ def main():
     # pair). For bf16 with H a multiple of 64 (>= 128) the row gather is folded
     # into the gate/up GEMM; otherwise permute also copies the rows.
     fused_gather = cfg.dtype == "bf16" and cfg.H % 64 == 0 and cfg.H >= 128 \
-        and cfg.T * cfg.H * 2 < 2 ** 31
+        and cfg.T * cfg.H * 2 < 2 ** 31 and not cfg.routing_on_input
     permute_bytes = 2 * 5 * P + 4 * P + 4 * P_in
     if not fused_gather:
         permute_bytes += cfg.T * cfg.H * eb + P_in * cfg.H * eb
     combine_bytes = P_in * cfg.H * eb + 8 * P + cfg.T * cfg.H * eb
+    if cfg.shared_expert:
+        combine_bytes += cfg.T * cfg.H * eb
     # GEMM floor: the larger of the compute time at peak and the time to stream
     # every slot's weights plus the activations (x or x_perm read, A written and
     # read, Y written) at HBM peak.

@@ -179,6 +179,24 @@ moe_status_t moe_slot_map(const int32_t* ids, const float* w, int T, int K, int 
  * x_perm may be NULL to compute only the index arrays.
  */
 size_t moe_permute_workspace_size(int T, int K, int S);
+
+/*
+ * moe_permute_scaled -- moe_permute whose gathered rows carry the routing
+ * weight: x_perm[pair_row[p]] = round(pair_w[p] * x[p / K]) (f32 product,
+ * one rounding to dt), for input-side routing.
+ *   Source: [A2A] review of torch_moe.py: _template_moe's
+ *   apply_routing_on_input, which applies the routing weights to the experts'
+ *   input instead of their output (a different result: the MLP is not
+ *   linear); the combine then uses weight 1 (moe_combine_shared with
+ *   w_masked = NULL).
+ * Arguments as moe_permute plus pair_w [T*K] f32 (the masked weights from
+ * moe_slot_map); x_perm must not be NULL.
+ */
+moe_status_t moe_permute_scaled(const void* x, moe_dtype_t dt, int T, int H, int K,
+                                const int32_t* slot, const uint8_t* mask, int S,
+                                const float* pair_w, int32_t* offsets, int32_t* sorted_pairs,
+                                int32_t* pair_row, void* x_perm, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
 moe_status_t moe_permute(const void* x, moe_dtype_t dt, int T, int H, int K,
                          const int32_t* slot, const uint8_t* mask, int S, int32_t* offsets,
                          int32_t* sorted_pairs, int32_t* pair_row, void* x_perm, void* ws,
@@ -226,6 +244,20 @@ moe_status_t moe_combine(const void* y, moe_dtype_t y_dt, const int32_t* pair_ro
                          const float* w_masked, int T, int K, int H, void* out,
                          moe_dtype_t out_dt, int accumulate, hipStream_t stream);
 
+/*
+ * moe_combine_shared -- moe_combine with two options.
+ *   Source: [EPMASK] ep_reduce_output: out = routed_out + shared_out before
+ *   the layer's single reduction; [A2A] apply_routing_on_input (unit weights
+ *   on the output side).
+ * w_masked == NULL: every included pair has weight 1.
+ * shared != NULL ([T, H] of shared_dt): acc[t] += shared[t] (f32) before
+ *   the accumulate step and the single rounding.
+ */
+moe_status_t moe_combine_shared(const void* y, moe_dtype_t y_dt, const int32_t* pair_row,
+                                const float* w_masked, int T, int K, int H, const void* shared,
+                                moe_dtype_t shared_dt, void* out, moe_dtype_t out_dt,
+                                int accumulate, hipStream_t stream);
+
 /* Fused forward: one call enqueues every stage in order on one stream. */
 typedef struct {
   int T_max;        /* largest T the workspace is sized for ([A2A] max num tokens) */
@@ -243,6 +275,7 @@ typedef struct {
   int accumulate;   /* add into out instead of overwriting it */
   int num_expert_group; /* 0: plain top-K; else group-limited routing (moe_route_grouped) */
   int topk_group;       /* groups kept when num_expert_group > 0 */
+  int routing_on_input; /* apply the routing weights to the expert input (see moe_permute_scaled) */
 } moe_config_t;
 
 /* Stage boundaries at which moe_forward records the caller's events. */
@@ -267,6 +300,7 @@ typedef struct {
   const int32_t* rep_slots; /* [S] */
   void* out;                /* [T, H] out_dtype */
   hipEvent_t events[MOE_NUM_EVENTS]; /* optional; NULL entries are skipped */
+  const void* shared_out;   /* [T, H] dtype or NULL: shared-expert output added in the combine */
 } moe_forward_args_t;
 
 /*
@@ -277,7 +311,9 @@ typedef struct {
  * moe_forward -- route (or take topk_ids / topk_w), slot map, permute,
  * grouped GEMM 1, grouped GEMM 2 and combine, all enqueued on `stream`.
  * Routing from logits is moe_route, or moe_route_grouped when
- * cfg->num_expert_group > 0 (cfg->topk_group groups kept).
+ * cfg->num_expert_group > 0 (cfg->topk_group groups kept). With
+ * cfg->routing_on_input the permutation is moe_permute_scaled and the combine
+ * uses unit weights; args->shared_out, if given, is added in the combine.
  * Equivalent to calling the staged entry points in that order. Intermediate
  * activations are stored in cfg->dtype. The workspace layout is internal;
  * its contents on entry are ignored.

@@ -50,13 +50,13 @@ class _Config(ctypes.Structure):
     _fields_ = [("T_max", _i), ("T", _i), ("H", _i), ("I", _i), ("E_global", _i), ("K", _i),
                 ("renormalize", _i), ("ep_size", _i), ("ep_rank", _i), ("S", _i),
                 ("dtype", _i), ("out_dtype", _i), ("accumulate", _i),
-                ("num_expert_group", _i), ("topk_group", _i)]
+                ("num_expert_group", _i), ("topk_group", _i), ("routing_on_input", _i)]
 
 
 class _ForwardArgs(ctypes.Structure):
     _fields_ = [("x", _p), ("logits", _p), ("topk_ids", _p), ("topk_w", _p),
                 ("w_gate_up", _p), ("w_down", _p), ("rep_off", _p), ("rep_slots", _p),
-                ("out", _p), ("events", _p * NUM_EVENTS)]
+                ("out", _p), ("events", _p * NUM_EVENTS), ("shared_out", _p)]
 
 
 _SIGS = {
@@ -66,8 +66,11 @@ _SIGS = {
     "moe_slot_map": (_i, [_p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p]),
     "moe_permute_workspace_size": (_sz, [_i, _i, _i]),
     "moe_permute": (_i, [_p, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_permute_scaled": (_i, [_p, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p, _p, _sz,
+                                _p]),
     "moe_grouped_gemm": (_i, [_i, _i, _p, _p, _i, _i, _p, _i, _i, _p, _p]),
     "moe_combine": (_i, [_p, _i, _p, _p, _i, _i, _i, _p, _i, _i, _p]),
+    "moe_combine_shared": (_i, [_p, _i, _p, _p, _i, _i, _i, _p, _i, _p, _i, _i, _p]),
     "moe_forward_workspace_size": (_sz, [ctypes.POINTER(_Config)]),
     "moe_forward": (_i, [ctypes.POINTER(_Config), ctypes.POINTER(_ForwardArgs), _p, _sz, _p]),
     "moe_a2a_dispatch_workspace_size": (_sz, [_i, _i, _i]),
@@ -190,10 +193,12 @@ def permute_workspace_size(T: int, K: int, S: int) -> int:
 
 
 def permute(x: torch.Tensor, slot: torch.Tensor, mask: torch.Tensor, S: int,
-            gather: bool = True, ws: Optional[torch.Tensor] = None):
+            gather: bool = True, ws: Optional[torch.Tensor] = None,
+            pair_w: Optional[torch.Tensor] = None):
     """moe_permute -> (offsets [S+1], sorted_pairs [T*K], pair_row [T*K], x_perm [T*K, H] or None).
 
-    Only rows [0, offsets[S]) of x_perm and sorted_pairs are written."""
+    Only rows [0, offsets[S]) of x_perm and sorted_pairs are written. With
+    pair_w [T, K] f32 (moe_permute_scaled) each row is pair_w[p] * x[p / K]."""
     _dev(x, "x", (torch.float32, torch.bfloat16))
     _dev(slot, "slot", torch.int32)
     T, K = slot.shape
@@ -208,9 +213,20 @@ def permute(x: torch.Tensor, slot: torch.Tensor, mask: torch.Tensor, S: int,
     need = permute_workspace_size(T, K, S)
     if ws is None:
         ws = _empty((max(need, 1),), torch.uint8, x)
-    _check(lib().moe_permute(_ptr(x), _DT[x.dtype], T, H, K, _ptr(slot), _ptr(mask), S,
-                             _ptr(offsets), _ptr(sorted_pairs), _ptr(pair_row), _ptr(x_perm),
-                             _ptr(ws), ws.numel() * ws.element_size(), _stream()), "moe_permute")
+    if pair_w is not None:
+        _dev(pair_w, "pair_w", torch.float32, (T, K))
+        if x_perm is None:
+            raise ValueError("pair_w needs the row gather")
+        _check(lib().moe_permute_scaled(_ptr(x), _DT[x.dtype], T, H, K, _ptr(slot), _ptr(mask),
+                                        S, _ptr(pair_w), _ptr(offsets), _ptr(sorted_pairs),
+                                        _ptr(pair_row), _ptr(x_perm), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream()),
+               "moe_permute_scaled")
+    else:
+        _check(lib().moe_permute(_ptr(x), _DT[x.dtype], T, H, K, _ptr(slot), _ptr(mask), S,
+                                 _ptr(offsets), _ptr(sorted_pairs), _ptr(pair_row),
+                                 _ptr(x_perm), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream()), "moe_permute")
     return offsets, sorted_pairs, pair_row, x_perm
 
 
@@ -247,16 +263,21 @@ def grouped_gemm(op: int, a: torch.Tensor, offsets: torch.Tensor, w: torch.Tenso
     return c
 
 
-def combine(y: torch.Tensor, pair_row: torch.Tensor, w_masked: torch.Tensor, K: int,
+def combine(y: torch.Tensor, pair_row: torch.Tensor, w_masked: Optional[torch.Tensor], K: int,
             out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
-            accumulate: bool = False) -> torch.Tensor:
-    """moe_combine: out[t] (+)= sum_k w_masked[t,k] * y[pair_row[t,k]]."""
+            accumulate: bool = False, shared: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_combine: out[t] (+)= sum_k w_masked[t,k] * y[pair_row[t,k]].
+    w_masked None (unit weights) or shared [T, H] (added before the rounding)
+    use moe_combine_shared."""
     _dev(y, "y", (torch.float32, torch.bfloat16))
     _dev(pair_row, "pair_row", torch.int32)
-    _dev(w_masked, "w_masked", torch.float32)
     P = pair_row.numel()
-    if P % K != 0 or w_masked.numel() != P:
-        raise ValueError("pair_row / w_masked must hold T*K entries")
+    if w_masked is not None:
+        _dev(w_masked, "w_masked", torch.float32)
+        if w_masked.numel() != P:
+            raise ValueError("pair_row / w_masked must hold T*K entries")
+    if P % K != 0:
+        raise ValueError("pair_row must hold T*K entries")
     T = P // K
     H = y.shape[1]
     if out is None:
@@ -265,9 +286,18 @@ def combine(y: torch.Tensor, pair_row: torch.Tensor, w_masked: torch.Tensor, K: 
             out.zero_()
     else:
         _dev(out, "out", (torch.float32, torch.bfloat16), (T, H))
-    _check(lib().moe_combine(_ptr(y), _DT[y.dtype], _ptr(pair_row), _ptr(w_masked), T, K, H,
-                             _ptr(out), _DT[out.dtype], int(bool(accumulate)), _stream()),
-           "moe_combine")
+    if w_masked is None or shared is not None:
+        sdt = MOE_DTYPE_BF16
+        if shared is not None:
+            _dev(shared, "shared", (torch.float32, torch.bfloat16), (T, H))
+            sdt = _DT[shared.dtype]
+        _check(lib().moe_combine_shared(_ptr(y), _DT[y.dtype], _ptr(pair_row), _ptr(w_masked), T,
+                                        K, H, _ptr(shared), sdt, _ptr(out), _DT[out.dtype],
+                                        int(bool(accumulate)), _stream()), "moe_combine_shared")
+    else:
+        _check(lib().moe_combine(_ptr(y), _DT[y.dtype], _ptr(pair_row), _ptr(w_masked), T, K,
+                                 H, _ptr(out), _DT[out.dtype], int(bool(accumulate)),
+                                 _stream()), "moe_combine")
     return out
 
 
@@ -278,19 +308,21 @@ class ForwardConfig:
     def __init__(self, T: int, H: int, I: int, E_global: int, K: int, renormalize: bool,
                  S: int, dtype: torch.dtype, out_dtype: Optional[torch.dtype] = None,
                  ep_size: int = 1, ep_rank: int = 0, accumulate: bool = False,
-                 T_max: Optional[int] = None, num_expert_group: int = 0, topk_group: int = 0):
+                 T_max: Optional[int] = None, num_expert_group: int = 0, topk_group: int = 0,
+                 routing_on_input: bool = False):
         self.T, self.H, self.I, self.E_global, self.K = T, H, I, E_global, K
         self.renormalize, self.S, self.dtype = bool(renormalize), S, dtype
         self.out_dtype = out_dtype or dtype
         self.ep_size, self.ep_rank, self.accumulate = ep_size, ep_rank, bool(accumulate)
         self.T_max = T if T_max is None else T_max
         self.num_expert_group, self.topk_group = num_expert_group, topk_group
+        self.routing_on_input = bool(routing_on_input)
 
     def c_struct(self) -> _Config:
         return _Config(self.T_max, self.T, self.H, self.I, self.E_global, self.K,
                        int(self.renormalize), self.ep_size, self.ep_rank, self.S,
                        _DT[self.dtype], _DT[self.out_dtype], int(self.accumulate),
-                       self.num_expert_group, self.topk_group)
+                       self.num_expert_group, self.topk_group, int(self.routing_on_input))
 
 
 def forward_workspace_size(cfg: ForwardConfig) -> int:
@@ -305,8 +337,8 @@ def forward(cfg: ForwardConfig, x: torch.Tensor, w_gate_up: torch.Tensor, w_down
             logits: Optional[torch.Tensor] = None, topk_ids: Optional[torch.Tensor] = None,
             topk_w: Optional[torch.Tensor] = None, rep_off: Optional[torch.Tensor] = None,
             rep_slots: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-            ws: Optional[torch.Tensor] = None, events: Optional[Sequence[int]] = None
-            ) -> torch.Tensor:
+            ws: Optional[torch.Tensor] = None, events: Optional[Sequence[int]] = None,
+            shared_out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """moe_forward. Pass logits [T, E_global] f32, or topk_ids [T, K] int32 and
     topk_w [T, K] f32. Weights are per slot: w_gate_up [S, 2I, H], w_down [S, H, I].
     `events`: up to NUM_EVENTS raw hipEvent_t handles (0 = skip) recorded at the
@@ -336,8 +368,11 @@ def forward(cfg: ForwardConfig, x: torch.Tensor, w_gate_up: torch.Tensor, w_down
     if events is not None:
         for i, e in enumerate(list(events)[:NUM_EVENTS]):
             ev[i] = e or 0
+    if shared_out is not None:
+        _dev(shared_out, "shared_out", cfg.dtype, (T, H))
     args = _ForwardArgs(_ptr(x), _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(w_gate_up),
-                        _ptr(w_down), _ptr(rep_off), _ptr(rep_slots), _ptr(out), ev)
+                        _ptr(w_down), _ptr(rep_off), _ptr(rep_slots), _ptr(out), ev,
+                        _ptr(shared_out))
     c = cfg.c_struct()
     _check(lib().moe_forward(ctypes.byref(c), ctypes.byref(args), _ptr(ws),
                              ws.numel() * ws.element_size(), _stream()), "moe_forward")

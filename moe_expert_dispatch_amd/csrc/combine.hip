@@ -6,7 +6,9 @@
 // (_template_moe applies the routing weights on the output side).
 //
 // Token-major: one block per token reads the token's K (row, weight) pairs
-// (weight 1 for every pair when no weights are given),
+// (weight 1 for every pair when no weights are given; with a shared-expert
+// output, [EPMASK] ep_reduce_output's out = routed_out + shared_out, its row
+// is added to the sum before the single rounding),
 // gathers the included expert-output rows with 16-byte loads, accumulates in
 // f32 in ascending k with fused multiply-adds and writes the token's output
 // row once. Every output element is written by exactly one thread, so the
@@ -89,7 +91,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
                                                       const int32_t* __restrict__ pair_row,
                                                       const float* __restrict__ w_masked, int K,
                                                       int H, OT* __restrict__ out,
-                                                      int accumulate) {
+                                                      int accumulate,
+                                                      const void* __restrict__ shared,
+                                                      int shared_bf16) {
   const int t = blockIdx.x;
   __shared__ int32_t rows[MOE_MAX_TOPK];
   __shared__ float wts[MOE_MAX_TOPK];
@@ -137,6 +141,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
     for (int u = 0; u < kVec; ++u) {
       const int v = v0 + u * blockDim.x;
       if (v >= nvec) continue;
+      if (shared != nullptr) {
+        float sv[8];
+        if (shared_bf16)
+          load8(static_cast<const uint16_t*>(shared) + (size_t)t * H + v * 8, sv);
+        else
+          load8(static_cast<const float*>(shared) + (size_t)t * H + v * 8, sv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[u][i] = acc[u][i] + sv[i];
+      }
       if (accumulate) {
         float prev[8];
         load8(o + v * 8, prev);
@@ -150,27 +163,35 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
 
 template <typename YT, typename OT>
 void launch_typed(const void* y, const int32_t* pair_row, const float* w_masked, int T, int K,
-                  int H, void* out, int accumulate, hipStream_t stream) {
+                  int H, void* out, int accumulate, const void* shared, int shared_bf16,
+                  hipStream_t stream) {
   combine_kernel<YT, OT, 8><<<T, 256, 0, stream>>>(static_cast<const YT*>(y), pair_row, w_masked,
-                                                   K, H, static_cast<OT*>(out), accumulate);
+                                                   K, H, static_cast<OT*>(out), accumulate,
+                                                   shared, shared_bf16);
 }
 
 }  // namespace
 
 moe_status_t launch_combine(const void* y, moe_dtype_t y_dt, const int32_t* pair_row,
                             const float* w_masked, int T, int K, int H, void* out,
-                            moe_dtype_t out_dt, int accumulate, hipStream_t stream) {
+                            moe_dtype_t out_dt, int accumulate, hipStream_t stream,
+                            const void* shared, moe_dtype_t shared_dt) {
   if (T == 0) return MOE_OK;
   const bool yb = y_dt == MOE_DTYPE_BF16;
   const bool ob = out_dt == MOE_DTYPE_BF16;
+  const int sb = shared_dt == MOE_DTYPE_BF16 ? 1 : 0;
   if (yb && ob)
-    launch_typed<uint16_t, uint16_t>(y, pair_row, w_masked, T, K, H, out, accumulate, stream);
+    launch_typed<uint16_t, uint16_t>(y, pair_row, w_masked, T, K, H, out, accumulate, shared, sb,
+                                     stream);
   else if (yb)
-    launch_typed<uint16_t, float>(y, pair_row, w_masked, T, K, H, out, accumulate, stream);
+    launch_typed<uint16_t, float>(y, pair_row, w_masked, T, K, H, out, accumulate, shared, sb,
+                                  stream);
   else if (ob)
-    launch_typed<float, uint16_t>(y, pair_row, w_masked, T, K, H, out, accumulate, stream);
+    launch_typed<float, uint16_t>(y, pair_row, w_masked, T, K, H, out, accumulate, shared, sb,
+                                  stream);
   else
-    launch_typed<float, float>(y, pair_row, w_masked, T, K, H, out, accumulate, stream);
+    launch_typed<float, float>(y, pair_row, w_masked, T, K, H, out, accumulate, shared, sb,
+                               stream);
   return launch_status();
 }
 

@@ -82,11 +82,13 @@ struct PermutePlan {
 };
 PermutePlan permute_plan(int T, int K, int S);
 // seg_cap > 0 places slot s's rows in the fixed block [s * seg_cap,
-// (s + 1) * seg_cap) (the caller guarantees every slot fits).
+// (s + 1) * seg_cap) (the caller guarantees every slot fits). pair_w non-null:
+// the row of pair p is pair_w[p] * x[p / K] (f32 product, rounded once).
 moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
                             const int32_t* slot, const uint8_t* mask, int S, int32_t* offsets,
                             int32_t* sorted_pairs, int32_t* pair_row, void* x_perm, void* ws,
-                            hipStream_t stream, int seg_cap = 0);
+                            hipStream_t stream, int seg_cap = 0,
+                            const float* pair_w = nullptr);
 
 moe_status_t launch_gemm_bf16(moe_gemm_op_t op, const void* a, const int32_t* offsets, int S,
                               int max_rows, const void* w, int H, int I, void* c,
@@ -115,9 +117,11 @@ moe_status_t launch_a2a_dispatch(const void* x, int elem_bytes, int T, int H, in
                                  void* send_x, int32_t* send_ids, float* send_w, void* ws,
                                  hipStream_t stream);
 
-// w_masked may be null: every pair then has weight 1.
+// w_masked may be null: every pair then has weight 1. shared (non-null,
+// [T, H] of shared_dt) is added to the token's sum before the rounding.
 moe_status_t launch_combine(const void* y, moe_dtype_t y_dt, const int32_t* pair_row,
                             const float* w_masked, int T, int K, int H, void* out,
-                            moe_dtype_t out_dt, int accumulate, hipStream_t stream);
+                            moe_dtype_t out_dt, int accumulate, hipStream_t stream,
+                            const void* shared = nullptr, moe_dtype_t shared_dt = MOE_DTYPE_BF16);
 
 }  // namespace moe

@@ -96,13 +96,15 @@ moe_status_t check_gemm(moe_gemm_op_t op, moe_dtype_t dt, const void* a, const i
   return MOE_OK;
 }
 
+// weights_required: moe_combine needs w_masked; moe_combine_shared accepts NULL.
 moe_status_t check_combine(const void* y, moe_dtype_t y_dt, const int32_t* pair_row,
                            const float* w_masked, int T, int K, int H, const void* out,
-                           moe_dtype_t out_dt) {
+                           moe_dtype_t out_dt, bool weights_required = true) {
   if (T < 0 || K < 1 || H < 1) return MOE_ERR_INVALID_ARG;
   if (!dtype_ok(y_dt) || !dtype_ok(out_dt)) return MOE_ERR_UNSUPPORTED;
   if (K > MOE_MAX_TOPK || H % 8 != 0 || !pairs_fit(T, K)) return MOE_ERR_UNSUPPORTED;
-  if (T > 0 && (!y || !pair_row || !w_masked || !out)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!y || !pair_row || !out)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && weights_required && !w_masked) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!aligned16(y) || !aligned16(out))) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
@@ -260,6 +262,19 @@ moe_status_t moe_permute(const void* x, moe_dtype_t dt, int T, int H, int K,
                         pair_row, x_perm, ws, stream);
 }
 
+moe_status_t moe_permute_scaled(const void* x, moe_dtype_t dt, int T, int H, int K,
+                                const int32_t* slot, const uint8_t* mask, int S,
+                                const float* pair_w, int32_t* offsets, int32_t* sorted_pairs,
+                                int32_t* pair_row, void* x_perm, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  const moe_status_t st = check_permute(x, dt, T, H, K, slot, mask, S, offsets, sorted_pairs,
+                                        pair_row, x_perm, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (T > 0 && (!pair_w || !x_perm)) return MOE_ERR_INVALID_ARG;
+  return launch_permute(x, dtype_bytes(dt), T, H, K, slot, mask, S, offsets, sorted_pairs,
+                        pair_row, x_perm, ws, stream, 0, pair_w);
+}
+
 moe_status_t moe_grouped_gemm(moe_gemm_op_t op, moe_dtype_t dt, const void* a,
                               const int32_t* offsets, int S, int max_rows, const void* w, int H,
                               int I, void* c, hipStream_t stream) {
@@ -274,6 +289,19 @@ moe_status_t moe_combine(const void* y, moe_dtype_t y_dt, const int32_t* pair_ro
   const moe_status_t st = check_combine(y, y_dt, pair_row, w_masked, T, K, H, out, out_dt);
   if (st != MOE_OK) return st;
   return launch_combine(y, y_dt, pair_row, w_masked, T, K, H, out, out_dt, accumulate, stream);
+}
+
+moe_status_t moe_combine_shared(const void* y, moe_dtype_t y_dt, const int32_t* pair_row,
+                                const float* w_masked, int T, int K, int H, const void* shared,
+                                moe_dtype_t shared_dt, void* out, moe_dtype_t out_dt,
+                                int accumulate, hipStream_t stream) {
+  const moe_status_t st =
+      check_combine(y, y_dt, pair_row, w_masked, T, K, H, out, out_dt, false);
+  if (st != MOE_OK) return st;
+  if (shared && !dtype_ok(shared_dt)) return MOE_ERR_UNSUPPORTED;
+  if (shared && T > 0 && !aligned16(shared)) return MOE_ERR_INVALID_ARG;
+  return launch_combine(y, y_dt, pair_row, w_masked, T, K, H, out, out_dt, accumulate, stream,
+                        shared, shared_dt);
 }
 
 size_t moe_forward_workspace_size(const moe_config_t* cfg) {
@@ -296,6 +324,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_forward_args_t* args
     if (!aligned16(args->x) || !aligned16(args->w_gate_up) || !aligned16(args->w_down) ||
         !aligned16(args->out))
       return MOE_ERR_INVALID_ARG;
+    if (args->shared_out && !aligned16(args->shared_out)) return MOE_ERR_INVALID_ARG;
   }
   const ForwardLayout L = forward_layout(cfg);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
@@ -340,10 +369,13 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_forward_args_t* args
   MOE_TRY(mark(MOE_EV_ROUTED));
   // bf16 with a direct-to-LDS shape: the gate/up GEMM fetches token rows of x
   // itself, so the permutation only orders the pairs (no x_perm copy).
-  const bool fused_gather = cfg->dtype == MOE_DTYPE_BF16 && gemm_bf16_gather_ok(T, H);
+  // Input-side routing gathers rows scaled by the pair weight instead.
+  const bool on_input = cfg->routing_on_input != 0;
+  const bool fused_gather =
+      !on_input && cfg->dtype == MOE_DTYPE_BF16 && gemm_bf16_gather_ok(T, H);
   MOE_TRY(launch_permute(args->x, dtype_bytes(cfg->dtype), T, H, K, slot, mask, S, offsets,
                          sorted_pairs, pair_row, fused_gather ? nullptr : x_perm, perm_ws,
-                         stream));
+                         stream, 0, on_input ? w_masked : nullptr));
   MOE_TRY(mark(MOE_EV_PERMUTED));
   if (fused_gather)
     MOE_TRY(launch_gemm_bf16_gate_up_gathered(args->x, T, K, sorted_pairs, offsets, S, T * K,
@@ -355,8 +387,9 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_forward_args_t* args
   MOE_TRY(launch_gemm(MOE_GEMM_DOWN, cfg->dtype, act, offsets, S, T * K, args->w_down, H, I, y,
                       stream));
   MOE_TRY(mark(MOE_EV_DOWN));
-  MOE_TRY(launch_combine(y, cfg->dtype, pair_row, w_masked, T, K, H, args->out, cfg->out_dtype,
-                         cfg->accumulate, stream));
+  MOE_TRY(launch_combine(y, cfg->dtype, pair_row, on_input ? nullptr : w_masked, T, K, H,
+                         args->out, cfg->out_dtype, cfg->accumulate, stream, args->shared_out,
+                         cfg->dtype));
   MOE_TRY(mark(MOE_EV_COMBINED));
 #undef MOE_TRY
   return MOE_OK;

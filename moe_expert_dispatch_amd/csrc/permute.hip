@@ -217,6 +217,47 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x
   }
 }
 
+// Input-side routing: the row of pair (t, k) is x[t] scaled by the pair's
+// weight, w * x evaluated in f32 and rounded once to the element type.
+__device__ __forceinline__ uint4 scale_row(uint4 v, float s, const uint16_t*) {
+  uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    q[i] = pack_bf16x2(bf16_to_f32(q[i] & 0xffffu) * s, bf16_to_f32(q[i] >> 16) * s);
+  return make_uint4(q[0], q[1], q[2], q[3]);
+}
+
+__device__ __forceinline__ uint4 scale_row(uint4 v, float s, const float*) {
+  return make_uint4(__float_as_uint(__uint_as_float(v.x) * s),
+                    __float_as_uint(__uint_as_float(v.y) * s),
+                    __float_as_uint(__uint_as_float(v.z) * s),
+                    __float_as_uint(__uint_as_float(v.w) * s));
+}
+
+template <typename ET>
+__global__ __launch_bounds__(256) void gather_scaled_kernel(const uint4* __restrict__ x, int T,
+                                                            int nvec, int K,
+                                                            const int32_t* __restrict__ pair_row,
+                                                            const float* __restrict__ pair_w,
+                                                            uint4* __restrict__ x_perm) {
+  const int t = blockIdx.x;
+  __shared__ int32_t rows[MOE_MAX_TOPK];
+  __shared__ float ws[MOE_MAX_TOPK];
+  if (threadIdx.x < K) {
+    rows[threadIdx.x] = pair_row[(size_t)t * K + threadIdx.x];
+    ws[threadIdx.x] = pair_w[(size_t)t * K + threadIdx.x];
+  }
+  __syncthreads();
+  const uint4* src = x + (size_t)t * nvec;
+  for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
+    const uint4 val = src[v];
+    for (int k = 0; k < K; ++k) {
+      const int r = rows[k];
+      if (r >= 0) x_perm[(size_t)r * nvec + v] = scale_row(val, ws[k], (const ET*)nullptr);
+    }
+  }
+}
+
 }  // namespace
 
 PermutePlan permute_plan(int T, int K, int S) {
@@ -237,7 +278,7 @@ PermutePlan permute_plan(int T, int K, int S) {
 moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
                             const int32_t* slot, const uint8_t* mask, int S, int32_t* offsets,
                             int32_t* sorted_pairs, int32_t* pair_row, void* x_perm, void* ws,
-                            hipStream_t stream, int seg_cap) {
+                            hipStream_t stream, int seg_cap, const float* pair_w) {
   const PermutePlan pl = permute_plan(T, K, S);
   int32_t* hist = static_cast<int32_t*>(ws);
   const size_t lds = (size_t)S * sizeof(int32_t);
@@ -254,8 +295,15 @@ moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
   }
   if (x_perm != nullptr && T > 0) {
     const int nvec = H * elem_bytes / 16;
-    gather_kernel<<<T, 256, 0, stream>>>(static_cast<const uint4*>(x), T, nvec, K, pair_row,
-                                         static_cast<uint4*>(x_perm));
+    const uint4* x4 = static_cast<const uint4*>(x);
+    uint4* xp4 = static_cast<uint4*>(x_perm);
+    if (pair_w == nullptr)
+      gather_kernel<<<T, 256, 0, stream>>>(x4, T, nvec, K, pair_row, xp4);
+    else if (elem_bytes == 2)
+      gather_scaled_kernel<uint16_t><<<T, 256, 0, stream>>>(x4, T, nvec, K, pair_row, pair_w,
+                                                            xp4);
+    else
+      gather_scaled_kernel<float><<<T, 256, 0, stream>>>(x4, T, nvec, K, pair_row, pair_w, xp4);
   }
   return launch_status();
 }

@@ -148,6 +148,23 @@ def test_a2a_validation_and_workspace(so):
     assert g(None, 1, fake, 8, 2, 64, fake, 1, None) == INVALID
 
 
+def test_scaled_permute_and_shared_combine_validation(so):
+    fake = ctypes.c_void_p(256)
+    big = ctypes.c_size_t(1 << 30)
+    f = so.moe_permute_scaled
+    # pair_w missing, x_perm missing: rejected before any launch
+    assert f(fake, 1, 4, 64, 2, fake, fake, 4, None, fake, fake, fake, fake, fake, big,
+             None) == INVALID
+    assert f(fake, 1, 4, 64, 2, fake, fake, 4, fake, fake, fake, fake, None, fake, big,
+             None) == INVALID
+    g = so.moe_combine_shared
+    assert g(fake, 1, fake, None, 4, 0, 64, None, 1, fake, 1, 0, None) == INVALID   # K < 1
+    assert g(fake, 1, fake, None, 4, 2, 64, fake, 9, fake, 1, 0, None) == UNSUPPORTED
+    assert g(fake, 1, fake, None, 4, 2, 64, ctypes.c_void_p(264), 1, fake, 1, 0,
+             None) == INVALID  # misaligned shared rows
+    assert g(None, 1, fake, None, 4, 2, 64, None, 1, fake, 1, 0, None) == INVALID
+
+
 def _cfg(**kw):
     base = dict(T=16, H=64, I=64, E_global=8, K=2, renormalize=True, S=8,
                 dtype=__import__("torch").bfloat16)

@@ -41,6 +41,8 @@ class WorkloadConfig:
     seed: int = 0
     num_expert_group: int = 0  # group-limited routing: groups (0 = plain top-K)
     topk_group: int = 0        # groups kept
+    shared_expert: bool = False     # a shared-expert output [T, H] is added in the combine
+    routing_on_input: bool = False  # routing weights applied to the expert input
 
     @property
     def E_local(self) -> int:
@@ -72,6 +74,12 @@ CONFIGS = {
                        renormalize=True, dtype="bf16", router="gauss", ep_size=4),
         WorkloadConfig("redundant_slots_zipf", T=16384, H=4096, I=1024, E=64, K=8,
                        renormalize=True, dtype="bf16", router="zipf", n_replicated=16),
+        # the 60-expert layer with a shared-expert output added, and with the
+        # routing weights applied on the expert input
+        WorkloadConfig("qwen2_moe_shared_bf16", T=4096, H=2048, I=1408, E=60, K=4,
+                       renormalize=False, dtype="bf16", router="gauss", shared_expert=True),
+        WorkloadConfig("qwen2_moe_input_routing_bf16", T=4096, H=2048, I=1408, E=60, K=4,
+                       renormalize=False, dtype="bf16", router="gauss", routing_on_input=True),
         # the 160-expert layer routed with 8 groups of 20 experts, 3 groups kept
         WorkloadConfig("deepseek_v2_grouped_bf16", T=8192, H=5120, I=1536, E=160, K=6,
                        renormalize=True, dtype="bf16", router="gauss_bias", bias_std=0.5,
