@@ -661,15 +661,34 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma_kernel(
     for (int x = 0; x < 6; ++x) read8(x, f0a, f0b, smem_base + a_lane[0], smem_base + b_lane[0]);
 
     dstep(0, std::true_type{});
-    for (int d = 1; d < nd; ++d) dstep(d, std::false_type{});
-
-    vm_wait<0>();
-    wait_frags(f0a, f0b);
-    __builtin_amdgcn_s_barrier();
-    const int nxt = next_item(item + G, &rt, &ct);
-    WItem done = cur;
-    const bool has_next = nxt < total;
-    if (has_next) setup(rt, ct, cur);
+    int nxt;
+    WItem done;
+    bool has_next;
+    if constexpr (GATHER) {
+      // The next item is set up before the last slice, whose full wait then
+      // covers setup's index loads: they have completed before any epilogue
+      // store is issued. (A store can complete before an older load, so no
+      // wait may count across the stores.) The last slice's DMAs are out of
+      // range whatever item they name.
+      for (int d = 1; d < nd - 1; ++d) dstep(d, std::false_type{});
+      nxt = next_item(item + G, &rt, &ct);
+      done = cur;
+      has_next = nxt < total;
+      if (has_next) setup(rt, ct, cur);
+      dstep(nd - 1, std::false_type{});
+      vm_wait<0>();
+      wait_frags(f0a, f0b);
+      __builtin_amdgcn_s_barrier();
+    } else {
+      for (int d = 1; d < nd; ++d) dstep(d, std::false_type{});
+      vm_wait<0>();
+      wait_frags(f0a, f0b);
+      __builtin_amdgcn_s_barrier();
+      nxt = next_item(item + G, &rt, &ct);
+      done = cur;
+      has_next = nxt < total;
+      if (has_next) setup(rt, ct, cur);
+    }
     epilogue(done);
     if (has_next) {
       gather_offsets(cur);
