@@ -38,6 +38,9 @@ COMPILE_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 instructions stay off in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # loop heads start on 64-byte instruction-fetch boundaries: the GEMM's
+    # K-loop time otherwise depends on where the linker happens to place it
+    "-falign-loops=64",
     "-Wall", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]

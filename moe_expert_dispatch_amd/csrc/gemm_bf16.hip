@@ -435,7 +435,7 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma_kernel(
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;  // 0..7
-  const int wm = wave >> 2;      // 128-row half of the tile
+  const int wm = uniform(wave >> 2);  // 128-row half of the tile
   const int wn = wave & 3;       // quarter of the weight rows
   const size_t w_rows = (OP == 0) ? 2 * (size_t)N : (size_t)N;
   const int BN = (OP == 0) ? BROWS / 2 : BROWS;
@@ -647,6 +647,16 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma_kernel(
     }
   };
 
+  // A slice for waves whose rows are all padding (the lower 128 rows of an
+  // item with at most 128 rows): only their share of the operand DMAs and
+  // the barrier, no fragment reads or MFMAs.
+  auto pass_step = [&](int d) {
+    vm_wait<0>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int x = 0; x < 8; ++x) dma(cur, x, d + 2);
+  };
+
   int rt, ct;
   int item = next_item((G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b, &rt, &ct);
   if (item < total) {
@@ -655,41 +665,50 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma_kernel(
     issue_prologue(cur);
   }
   while (item < total) {
+    const bool skip = wm == 1 && cur.rows <= BM / 2;
     vm_wait<WDMA>();
     __builtin_amdgcn_s_barrier();
-#pragma unroll
-    for (int x = 0; x < 6; ++x) read8(x, f0a, f0b, smem_base + a_lane[0], smem_base + b_lane[0]);
-
-    dstep(0, std::true_type{});
-    int nxt;
+    int nxt = 0;
     WItem done;
-    bool has_next;
-    if constexpr (GATHER) {
-      // The next item is set up before the last slice, whose full wait then
-      // covers setup's index loads: they have completed before any epilogue
-      // store is issued. (A store can complete before an older load, so no
-      // wait may count across the stores.) The last slice's DMAs are out of
-      // range whatever item they name.
-      for (int d = 1; d < nd - 1; ++d) dstep(d, std::false_type{});
+    bool has_next = false;
+    auto next_setup = [&]() {
       nxt = next_item(item + G, &rt, &ct);
       done = cur;
       has_next = nxt < total;
       if (has_next) setup(rt, ct, cur);
-      dstep(nd - 1, std::false_type{});
+    };
+    // With the gather, the next item is set up before the last slice, whose
+    // full wait then covers setup's index loads: they have completed before
+    // any epilogue store is issued. (A store can complete before an older
+    // load, so no wait may count across the stores.) The last slice's DMAs
+    // are out of range whatever item they name.
+    const int dlast = GATHER ? nd - 1 : nd;
+    // The epilogue sits inside the computing branch, so the accumulators are
+    // not live across the pass-only slices.
+    if (!skip) {
+#pragma unroll
+      for (int x = 0; x < 6; ++x) read8(x, f0a, f0b, smem_base + a_lane[0], smem_base + b_lane[0]);
+      dstep(0, std::true_type{});
+      for (int d = 1; d < dlast; ++d) dstep(d, std::false_type{});
+      if constexpr (GATHER) {
+        next_setup();
+        dstep(nd - 1, std::false_type{});
+      }
       vm_wait<0>();
       wait_frags(f0a, f0b);
       __builtin_amdgcn_s_barrier();
+      if constexpr (!GATHER) next_setup();
+      epilogue(done);
     } else {
-      for (int d = 1; d < nd; ++d) dstep(d, std::false_type{});
+      for (int d = 0; d < dlast; ++d) pass_step(d);
+      if constexpr (GATHER) {
+        next_setup();
+        pass_step(nd - 1);
+      }
       vm_wait<0>();
-      wait_frags(f0a, f0b);
       __builtin_amdgcn_s_barrier();
-      nxt = next_item(item + G, &rt, &ct);
-      done = cur;
-      has_next = nxt < total;
-      if (has_next) setup(rt, ct, cur);
+      if constexpr (!GATHER) next_setup();
     }
-    epilogue(done);
     if (has_next) {
       gather_offsets(cur);
       issue_prologue(cur);
