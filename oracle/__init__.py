@@ -22,3 +22,14 @@ from .moe_oracle import (  # noqa: F401
     swiglu_mlp,
     topk_ids,
 )
+from .fp8_oracle import (  # noqa: F401
+    E4M3_MAX,
+    e4m3_decode,
+    e4m3_encode,
+    fp8_expert_mlp,
+    fp8_forward,
+    fp8_grouped_down,
+    fp8_grouped_gate_up,
+    fp8_linear,
+    quantize_fp8,
+)
