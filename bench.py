@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused-MoE layer tokens/sec; grouped-GEMM TFLOP/s as % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_F32_TFLOPS = 157.3  # MI355X fp32 vector (FMA) peak
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_traffic.json")
@@ -166,7 +167,11 @@ def cpu_baseline(inp, seconds, rank=0):
     t0 = time.perf_counter()
     while True:
         tok = np.arange(done, min(done + block, cfg.T))
-        if cfg.num_expert_group:
+        if cfg.dtype == "fp8":
+            oracle.fp8_forward(inp.x, inp.logits, inp.w_gate_up.numpy(), inp.w_gate_up_scale,
+                               inp.w_down.numpy(), inp.w_down_scale, cfg.a1_scale, cfg.a2_scale,
+                               cfg.K, cfg.renormalize, cfg.ep_size, rank, tokens=tok)
+        elif cfg.num_expert_group:
             ids, w = oracle.route_grouped(inp.logits.numpy()[tok], cfg.K, cfg.renormalize,
                                           cfg.num_expert_group, cfg.topk_group)
             oracle.forward(inp.x[tok], None, inp.w_gate_up, inp.w_down, cfg.K, False,
@@ -212,29 +217,35 @@ def main():
     if not 0 <= rank < cfg.ep_size:
         print(f"--ep-rank must be in [0, {cfg.ep_size}) for {cfg.name}", file=sys.stderr)
         sys.exit(2)
-    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    fp8 = cfg.dtype == "fp8"
+    tdt = torch.bfloat16 if cfg.dtype in ("bf16", "fp8") else torch.float32  # x and out
     t_gen = time.perf_counter()
     inp = make_inputs(cfg)
+    wgu_h, wd_h = inp.share_weights(rank)
+    sgu_h, sd_h = inp.share_scales(rank) if fp8 else (None, None)
     if cfg.n_replicated:
         ro, rs, se = build_slot_table(cfg.E_local, inp.replicated_experts())
-        wgu_h, wd_h = inp.share_weights(rank)
-        wgu = slot_weights(wgu_h, se).to(dev)
-        wd = slot_weights(wd_h, se).to(dev)
+        wgu_h, wd_h = slot_weights(wgu_h, se), slot_weights(wd_h, se)
+        if fp8:
+            sgu_h, sd_h = slot_weights(sgu_h, se), slot_weights(sd_h, se)
         S = int(se.numel())
     else:
         ro, rs = identity_slot_table(cfg.E_local)
-        wgu_h, wd_h = inp.share_weights(rank)
-        wgu, wd = wgu_h.contiguous().to(dev), wd_h.contiguous().to(dev)
         S = cfg.E_local
+    wgu, wd = wgu_h.contiguous().to(dev), wd_h.contiguous().to(dev)
+    sgu = sgu_h.contiguous().to(dev) if fp8 else None
+    sd = sd_h.contiguous().to(dev) if fp8 else None
     x = inp.x.to(dev)
     logits = inp.logits.to(dev)
     ro, rs = ro.to(dev), rs.to(dev)
     gen_s = time.perf_counter() - t_gen
 
     fc = moe.ForwardConfig(T=cfg.T, H=cfg.H, I=cfg.I, E_global=cfg.E, K=cfg.K,
-                           renormalize=cfg.renormalize, S=S, dtype=tdt, ep_size=cfg.ep_size,
+                           renormalize=cfg.renormalize, S=S, dtype=moe.FP8 if fp8 else tdt,
+                           out_dtype=tdt, ep_size=cfg.ep_size,
                            ep_rank=rank, num_expert_group=cfg.num_expert_group,
-                           topk_group=cfg.topk_group, routing_on_input=cfg.routing_on_input)
+                           topk_group=cfg.topk_group, routing_on_input=cfg.routing_on_input,
+                           a1_scale=cfg.a1_scale, a2_scale=cfg.a2_scale)
     shared = None
     if cfg.shared_expert:  # stands for the shared expert's output (not computed here)
         shared = torch.randn(cfg.T, cfg.H, generator=torch.Generator().manual_seed(1)).to(
@@ -250,7 +261,7 @@ def main():
 
     def step(events=None):
         moe.forward(fc, x, wgu, wd, logits=logits, rep_off=ro, rep_slots=rs, out=out, ws=ws,
-                    events=events, shared_out=shared)
+                    events=events, shared_out=shared, w_gate_up_scale=sgu, w_down_scale=sd)
 
     for _ in range(args.warmup):
         step()
@@ -277,7 +288,8 @@ def main():
             stage_ms[n] += row[j].elapsed_time(row[j + 1]) / args.steps
     ms_per_step = ev[0][0].elapsed_time(ev[-1][-1]) / args.steps
 
-    eb = 2 if cfg.dtype == "bf16" else 4
+    eb = {"bf16": 2, "fp8": 2, "f32": 4}[cfg.dtype]  # x, Y and out element bytes
+    wb = 1 if fp8 else eb                             # weight and A element bytes
     fl_gu = 4.0 * cfg.H * cfg.I * P_in       # gate and up products
     fl_dn = 2.0 * cfg.H * cfg.I * P_in
     gemm_tflops = (fl_gu + fl_dn) / ((stage_ms["gemm_gate_up"] + stage_ms["gemm_down"]) * 1e9)
@@ -287,21 +299,23 @@ def main():
     # scatter writes pair_row (4 B per pair) and sorted_pairs (4 B per included
     # pair). For bf16 with H a multiple of 64 (>= 128) the row gather is folded
     # into the gate/up GEMM; otherwise permute also copies the rows.
-    fused_gather = cfg.dtype == "bf16" and cfg.H % 64 == 0 and cfg.H >= 128 \
-        and cfg.T * cfg.H * 2 < 2 ** 31 and not cfg.routing_on_input
+    fused_gather = fp8 or (cfg.dtype == "bf16" and cfg.H % 64 == 0 and cfg.H >= 128
+                           and cfg.T * cfg.H * 2 < 2 ** 31 and not cfg.routing_on_input)
     permute_bytes = 2 * 5 * P + 4 * P + 4 * P_in
     if not fused_gather:
         permute_bytes += cfg.T * cfg.H * eb + P_in * cfg.H * eb
+    if fp8:  # the permute stage also quantizes x (read bf16, write codes)
+        permute_bytes += cfg.T * cfg.H * (2 + 1)
     combine_bytes = P_in * cfg.H * eb + 8 * P + cfg.T * cfg.H * eb
     if cfg.shared_expert:
         combine_bytes += cfg.T * cfg.H * eb
     # GEMM floor: the larger of the compute time at peak and the time to stream
     # every slot's weights plus the activations (x or x_perm read, A written and
     # read, Y written) at HBM peak.
-    peak_tf = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
-    gemm_bytes = (S * 3 * cfg.H * cfg.I * eb
-                  + (cfg.T if fused_gather else P_in) * cfg.H * eb
-                  + 2 * P_in * cfg.I * eb + P_in * cfg.H * eb)
+    peak_tf = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS, "f32": PEAK_F32_TFLOPS}[cfg.dtype]
+    gemm_bytes = (S * 3 * cfg.H * cfg.I * wb
+                  + (cfg.T if fused_gather else P_in) * cfg.H * wb
+                  + 2 * P_in * cfg.I * wb + P_in * cfg.H * eb)
     gemm_floor_ms = max((fl_gu + fl_dn) / (peak_tf * 1e9), gemm_bytes / (PEAK_HBM_GBPS * 1e6))
     gemm_ms = stage_ms["gemm_gate_up"] + stage_ms["gemm_down"]
     traffic = gemm_traffic(cfg.name) if cfg.dtype == "bf16" else None
@@ -317,7 +331,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3", "f32": "f32"}[cfg.dtype],
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H,
                    "intermediate": cfg.I, "experts": cfg.E, "slots": S, "top_k": cfg.K,
@@ -327,11 +341,16 @@ def main():
                       "achieved": gu_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                       "frac": gu_tflops / PEAK_BF16_TFLOPS, "traffic": traffic}
                      if cfg.dtype == "bf16" else
+                     {"bound": "mfma", "kernel": "grouped_gemm fp8 (E4M3) gate/up + SwiGLU",
+                      "achieved": gu_tflops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                      "frac": gu_tflops / PEAK_FP8_TFLOPS, "traffic": None}
+                     if fp8 else
                      {"bound": "alu", "kernel": "grouped_gemm_f32 gate/up + SwiGLU (FMA)",
                       "achieved": gu_tflops, "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
                       "frac": gu_tflops / PEAK_F32_TFLOPS, "traffic": None}),
         "grouped_gemm_tflops": gemm_tflops,
         "grouped_gemm_frac_of_bf16_peak": gemm_tflops / PEAK_BF16_TFLOPS,
+        "grouped_gemm_frac_of_peak": gemm_tflops / peak_tf,
         "grouped_gemm_floor_ms": gemm_floor_ms,
         "grouped_gemm_frac_of_roofline": gemm_floor_ms / gemm_ms,
         "stage_ms": stage_ms,

@@ -71,7 +71,8 @@ typedef enum {
 
 typedef enum {
   MOE_DTYPE_F32 = 0,
-  MOE_DTYPE_BF16 = 1
+  MOE_DTYPE_BF16 = 1,
+  MOE_DTYPE_FP8_E4M3 = 2 /* OCP FP8 E4M3 codes (moe_quantize_fp8, moe_grouped_gemm_fp8) */
 } moe_dtype_t;
 
 typedef enum {
@@ -227,6 +228,50 @@ moe_status_t moe_grouped_gemm(moe_gemm_op_t op, moe_dtype_t dt, const void* a,
                               int H, int I, void* c, hipStream_t stream);
 
 /*
+ * FP8 (E4M3) expert MLP.
+ *   Source: [A2A] review of torch_moe.py: the FP8 (and NVFP4) MoE ops run
+ *   the same routed template (routing, gated MLP per expert, output-side
+ *   combine) with quantized expert linears. The pages give no quantization
+ *   scheme; the one implemented here:
+ *   - codes are OCP FP8 E4M3: s eeee mmm, value (-1)^s 2^(e-7) (1 + m/8) for
+ *     e > 0, (-1)^s 2^-6 (m/8) for e = 0; s 1111 111 is NaN; max 448;
+ *   - quantize(v, scale) = the E4M3 value nearest to
+ *     clamp(fl32(v * fl32(1 / scale)), -448, 448), ties to the even code;
+ *   - activations carry one scale per tensor, fixed ahead of time: a1 for
+ *     the expert input x, a2 for the SwiGLU output; weights carry one scale
+ *     per slot and matrix: w_scale[s] for the stacked gate/up rows, another
+ *     array for down;
+ *   - a linear layer computes (s_in * s_w) * sum_k dec(q_in[k]) dec(q_w[n,k])
+ *     with f32 accumulation of the exact code products.
+ */
+
+/*
+ * moe_quantize_fp8 -- q[i] = quantize(x[i], scale) for i < n.
+ * x of x_dt (MOE_DTYPE_BF16 or MOE_DTYPE_F32) and q (bytes) are device
+ * buffers, 16-byte aligned; scale must be finite and > 0. x must hold
+ * finite values (a NaN input gives an unspecified code).
+ */
+moe_status_t moe_quantize_fp8(const void* x, moe_dtype_t x_dt, int64_t n, float scale,
+                              uint8_t* q, hipStream_t stream);
+
+/*
+ * moe_grouped_gemm_fp8 -- moe_grouped_gemm on E4M3 codes.
+ * a: codes [rows, H] (gate/up) or [rows, I] (down), scale a_scale; w: codes
+ * laid out as for moe_grouped_gemm, slot s scaled by w_scale[s] (device f32
+ * array [S]). op == MOE_GEMM_GATE_UP_SWIGLU: c holds codes [rows, I] of
+ * quantize(silu(g) * u, c_scale), the SwiGLU evaluated in f32 on the scaled
+ * accumulators g, u. op == MOE_GEMM_DOWN: c is bf16 [rows, H], the scaled
+ * accumulator rounded once (c_scale unused). The contraction length (H for
+ * gate/up, I for down) must be a multiple of 128 and at least 256
+ * (MOE_ERR_UNSUPPORTED otherwise); scales finite and > 0; a, w, c 16-byte
+ * aligned.
+ */
+moe_status_t moe_grouped_gemm_fp8(moe_gemm_op_t op, const uint8_t* a, float a_scale,
+                                  const int32_t* offsets, int S, int max_rows, const uint8_t* w,
+                                  const float* w_scale, int H, int I, void* c, float c_scale,
+                                  hipStream_t stream);
+
+/*
  * moe_combine -- weighted sum back into token order.
  *   Source: [AUTOTP] the routed output is the weighted sum of the selected
  *   experts' outputs, completed before the single reduction of the layer;
@@ -276,6 +321,8 @@ typedef struct {
   int num_expert_group; /* 0: plain top-K; else group-limited routing (moe_route_grouped) */
   int topk_group;       /* groups kept when num_expert_group > 0 */
   int routing_on_input; /* apply the routing weights to the expert input (see moe_permute_scaled) */
+  float a1_scale;       /* dtype MOE_DTYPE_FP8_E4M3: scale of the quantized expert input */
+  float a2_scale;       /* dtype MOE_DTYPE_FP8_E4M3: scale of the quantized SwiGLU output */
 } moe_config_t;
 
 /* Stage boundaries at which moe_forward records the caller's events. */
@@ -301,6 +348,8 @@ typedef struct {
   void* out;                /* [T, H] out_dtype */
   hipEvent_t events[MOE_NUM_EVENTS]; /* optional; NULL entries are skipped */
   const void* shared_out;   /* [T, H] dtype or NULL: shared-expert output added in the combine */
+  const float* w_gate_up_scale; /* dtype MOE_DTYPE_FP8_E4M3: [S] scales of w_gate_up */
+  const float* w_down_scale;    /* dtype MOE_DTYPE_FP8_E4M3: [S] scales of w_down */
 } moe_forward_args_t;
 
 /*
@@ -317,6 +366,13 @@ typedef struct {
  * Equivalent to calling the staged entry points in that order. Intermediate
  * activations are stored in cfg->dtype. The workspace layout is internal;
  * its contents on entry are ignored.
+ * cfg->dtype == MOE_DTYPE_FP8_E4M3: x (and shared_out) are bf16; w_gate_up
+ * and w_down are E4M3 codes with per-slot scales args->w_gate_up_scale and
+ * args->w_down_scale; x is quantized with cfg->a1_scale (moe_quantize_fp8),
+ * the grouped GEMMs are moe_grouped_gemm_fp8 with the SwiGLU output
+ * quantized with cfg->a2_scale, and the expert outputs are bf16. H and I
+ * must be multiples of 128 and at least 256; routing_on_input is not
+ * supported with FP8 (MOE_ERR_UNSUPPORTED).
  */
 size_t moe_forward_workspace_size(const moe_config_t* cfg);
 moe_status_t moe_forward(const moe_config_t* cfg, const moe_forward_args_t* args, void* ws,

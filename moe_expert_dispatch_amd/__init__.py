@@ -31,6 +31,7 @@ _LIB_FILE = os.path.join(_HERE, "libmoe_hip.so")
 
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
+MOE_DTYPE_FP8_E4M3 = 2
 GATE_UP_SWIGLU = 0
 DOWN = 1
 NUM_EVENTS = 6
@@ -38,7 +39,10 @@ MAX_EXPERTS = 1024
 MAX_TOPK = 32
 MAX_SLOTS = 1024
 
-_DT = {torch.float32: MOE_DTYPE_F32, torch.bfloat16: MOE_DTYPE_BF16}
+_DT = {torch.float32: MOE_DTYPE_F32, torch.bfloat16: MOE_DTYPE_BF16,
+       torch.float8_e4m3fn: MOE_DTYPE_FP8_E4M3}
+FP8 = torch.float8_e4m3fn  # ForwardConfig dtype of the FP8 expert path
+_CODES = (torch.uint8, torch.float8_e4m3fn)  # tensors holding E4M3 codes
 _TORCH_DT = {MOE_DTYPE_F32: torch.float32, MOE_DTYPE_BF16: torch.bfloat16}
 
 _p = ctypes.c_void_p
@@ -50,13 +54,15 @@ class _Config(ctypes.Structure):
     _fields_ = [("T_max", _i), ("T", _i), ("H", _i), ("I", _i), ("E_global", _i), ("K", _i),
                 ("renormalize", _i), ("ep_size", _i), ("ep_rank", _i), ("S", _i),
                 ("dtype", _i), ("out_dtype", _i), ("accumulate", _i),
-                ("num_expert_group", _i), ("topk_group", _i), ("routing_on_input", _i)]
+                ("num_expert_group", _i), ("topk_group", _i), ("routing_on_input", _i),
+                ("a1_scale", ctypes.c_float), ("a2_scale", ctypes.c_float)]
 
 
 class _ForwardArgs(ctypes.Structure):
     _fields_ = [("x", _p), ("logits", _p), ("topk_ids", _p), ("topk_w", _p),
                 ("w_gate_up", _p), ("w_down", _p), ("rep_off", _p), ("rep_slots", _p),
-                ("out", _p), ("events", _p * NUM_EVENTS), ("shared_out", _p)]
+                ("out", _p), ("events", _p * NUM_EVENTS), ("shared_out", _p),
+                ("w_gate_up_scale", _p), ("w_down_scale", _p)]
 
 
 _SIGS = {
@@ -77,6 +83,9 @@ _SIGS = {
     "moe_a2a_dispatch": (_i, [_p, _i, _i, _i, _i, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _p,
                               _p, _sz, _p]),
     "moe_a2a_combine": (_i, [_p, _i, _p, _i, _i, _i, _p, _i, _p]),
+    "moe_quantize_fp8": (_i, [_p, _i, ctypes.c_int64, ctypes.c_float, _p, _p]),
+    "moe_grouped_gemm_fp8": (_i, [_i, _p, ctypes.c_float, _p, _i, _i, _p, _p, _i, _i, _p,
+                                  ctypes.c_float, _p]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -263,6 +272,53 @@ def grouped_gemm(op: int, a: torch.Tensor, offsets: torch.Tensor, w: torch.Tenso
     return c
 
 
+def quantize_fp8(x: torch.Tensor, scale: float, q: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_quantize_fp8: E4M3 codes (uint8, shape of x) of x (bf16 or f32) / scale."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    q = _empty(tuple(x.shape), torch.uint8, x) if q is None else _dev(q, "q", _CODES, x.shape)
+    _check(lib().moe_quantize_fp8(_ptr(x), _DT[x.dtype], x.numel(), float(scale), _ptr(q),
+                                  _stream()), "moe_quantize_fp8")
+    return q
+
+
+def grouped_gemm_fp8(op: int, a: torch.Tensor, a_scale: float, offsets: torch.Tensor,
+                     w: torch.Tensor, w_scale: torch.Tensor, c_scale: float = 1.0,
+                     c: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_grouped_gemm_fp8. Codes a [rows, H] / [rows, I] and w (as grouped_gemm),
+    f32 w_scale [S]. GATE_UP_SWIGLU -> codes [rows, I] quantized with c_scale;
+    DOWN -> bf16 [rows, H]."""
+    _dev(a, "a", _CODES)
+    _dev(w, "w", _CODES)
+    _dev(offsets, "offsets", torch.int32)
+    if a.dim() != 2 or w.dim() != 3:
+        raise ValueError("a must be 2-D and w 3-D")
+    S = w.shape[0]
+    _dev(w_scale, "w_scale", torch.float32, (S,))
+    if offsets.numel() != S + 1:
+        raise ValueError("offsets must have S + 1 entries")
+    rows = a.shape[0]
+    if op == GATE_UP_SWIGLU:
+        H, I = a.shape[1], w.shape[1] // 2
+        if w.shape[2] != H or w.shape[1] != 2 * I:
+            raise ValueError("w must be [S, 2I, H]")
+        shape, cdt = (rows, I), _CODES
+    elif op == DOWN:
+        I, H = a.shape[1], w.shape[1]
+        if w.shape[2] != I:
+            raise ValueError("w must be [S, H, I]")
+        shape, cdt = (rows, H), torch.bfloat16
+    else:
+        raise ValueError("op must be GATE_UP_SWIGLU or DOWN")
+    if c is None:
+        c = _empty(shape, torch.uint8 if op == GATE_UP_SWIGLU else torch.bfloat16, a)
+    else:
+        _dev(c, "c", cdt, shape)
+    _check(lib().moe_grouped_gemm_fp8(op, _ptr(a), float(a_scale), _ptr(offsets), S, rows,
+                                      _ptr(w), _ptr(w_scale), H, I, _ptr(c), float(c_scale),
+                                      _stream()), "moe_grouped_gemm_fp8")
+    return c
+
+
 def combine(y: torch.Tensor, pair_row: torch.Tensor, w_masked: Optional[torch.Tensor], K: int,
             out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
             accumulate: bool = False, shared: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -309,10 +365,12 @@ class ForwardConfig:
                  S: int, dtype: torch.dtype, out_dtype: Optional[torch.dtype] = None,
                  ep_size: int = 1, ep_rank: int = 0, accumulate: bool = False,
                  T_max: Optional[int] = None, num_expert_group: int = 0, topk_group: int = 0,
-                 routing_on_input: bool = False):
+                 routing_on_input: bool = False, a1_scale: float = 1.0, a2_scale: float = 1.0):
         self.T, self.H, self.I, self.E_global, self.K = T, H, I, E_global, K
         self.renormalize, self.S, self.dtype = bool(renormalize), S, dtype
-        self.out_dtype = out_dtype or dtype
+        # FP8 (dtype FP8): x, shared_out and the default out are bf16
+        self.out_dtype = out_dtype or (torch.bfloat16 if dtype == FP8 else dtype)
+        self.a1_scale, self.a2_scale = float(a1_scale), float(a2_scale)
         self.ep_size, self.ep_rank, self.accumulate = ep_size, ep_rank, bool(accumulate)
         self.T_max = T if T_max is None else T_max
         self.num_expert_group, self.topk_group = num_expert_group, topk_group
@@ -322,7 +380,8 @@ class ForwardConfig:
         return _Config(self.T_max, self.T, self.H, self.I, self.E_global, self.K,
                        int(self.renormalize), self.ep_size, self.ep_rank, self.S,
                        _DT[self.dtype], _DT[self.out_dtype], int(self.accumulate),
-                       self.num_expert_group, self.topk_group, int(self.routing_on_input))
+                       self.num_expert_group, self.topk_group, int(self.routing_on_input),
+                       self.a1_scale, self.a2_scale)
 
 
 def forward_workspace_size(cfg: ForwardConfig) -> int:
@@ -338,15 +397,25 @@ def forward(cfg: ForwardConfig, x: torch.Tensor, w_gate_up: torch.Tensor, w_down
             topk_w: Optional[torch.Tensor] = None, rep_off: Optional[torch.Tensor] = None,
             rep_slots: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
             ws: Optional[torch.Tensor] = None, events: Optional[Sequence[int]] = None,
-            shared_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+            shared_out: Optional[torch.Tensor] = None,
+            w_gate_up_scale: Optional[torch.Tensor] = None,
+            w_down_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
     """moe_forward. Pass logits [T, E_global] f32, or topk_ids [T, K] int32 and
     topk_w [T, K] f32. Weights are per slot: w_gate_up [S, 2I, H], w_down [S, H, I].
     `events`: up to NUM_EVENTS raw hipEvent_t handles (0 = skip) recorded at the
-    stage boundaries."""
+    stage boundaries. cfg.dtype FP8: x is bf16, the weights are E4M3 codes
+    (uint8 or float8_e4m3fn) with f32 per-slot scales w_gate_up_scale,
+    w_down_scale [S]."""
     T, H, I, S = cfg.T, cfg.H, cfg.I, cfg.S
-    _dev(x, "x", cfg.dtype, (T, H))
-    _dev(w_gate_up, "w_gate_up", cfg.dtype, (S, 2 * I, H))
-    _dev(w_down, "w_down", cfg.dtype, (S, H, I))
+    fp8 = cfg.dtype == FP8
+    xdt = torch.bfloat16 if fp8 else cfg.dtype
+    wdt = _CODES if fp8 else cfg.dtype
+    _dev(x, "x", xdt, (T, H))
+    _dev(w_gate_up, "w_gate_up", wdt, (S, 2 * I, H))
+    _dev(w_down, "w_down", wdt, (S, H, I))
+    if fp8:
+        _dev(w_gate_up_scale, "w_gate_up_scale", torch.float32, (S,))
+        _dev(w_down_scale, "w_down_scale", torch.float32, (S,))
     if logits is not None:
         _dev(logits, "logits", torch.float32, (T, cfg.E_global))
     else:
@@ -369,10 +438,10 @@ def forward(cfg: ForwardConfig, x: torch.Tensor, w_gate_up: torch.Tensor, w_down
         for i, e in enumerate(list(events)[:NUM_EVENTS]):
             ev[i] = e or 0
     if shared_out is not None:
-        _dev(shared_out, "shared_out", cfg.dtype, (T, H))
+        _dev(shared_out, "shared_out", xdt, (T, H))
     args = _ForwardArgs(_ptr(x), _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(w_gate_up),
                         _ptr(w_down), _ptr(rep_off), _ptr(rep_slots), _ptr(out), ev,
-                        _ptr(shared_out))
+                        _ptr(shared_out), _ptr(w_gate_up_scale), _ptr(w_down_scale))
     c = cfg.c_struct()
     _check(lib().moe_forward(ctypes.byref(c), ctypes.byref(args), _ptr(ws),
                              ws.numel() * ws.element_size(), _stream()), "moe_forward")

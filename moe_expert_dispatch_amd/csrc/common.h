@@ -106,6 +106,26 @@ moe_status_t launch_gemm_f32(moe_gemm_op_t op, const void* a, const int32_t* off
                              int max_rows, const void* w, int H, int I, void* c,
                              hipStream_t stream);
 
+// FP8 (E4M3) grouped GEMMs: a and w are codes, slot s's products are scaled by
+// a_scale * w_scale[s]. Gate/up writes the SwiGLU output as codes quantized
+// with out_scale; down writes bf16. Both need the contraction length to be a
+// multiple of 128 and at least 256 (gemm_fp8_ok).
+bool gemm_fp8_ok(int Kd);
+bool gemm_fp8_gather_ok(int T, int H);
+moe_status_t launch_gemm_fp8(moe_gemm_op_t op, const uint8_t* a, float a_scale,
+                             const int32_t* offsets, int S, int max_rows, const uint8_t* w,
+                             const float* w_scale, int H, int I, void* c, float out_scale,
+                             hipStream_t stream);
+moe_status_t launch_gemm_fp8_gate_up_gathered(const uint8_t* xq, int T, int K,
+                                              const int32_t* sorted_pairs,
+                                              const int32_t* offsets, int S, int max_rows,
+                                              const uint8_t* w, const float* w_scale,
+                                              float a_scale, int H, int I, void* c,
+                                              float out_scale, hipStream_t stream);
+// q[i] = E4M3 code of clamp(x[i] * (1 / scale), -448, 448), rounded to nearest even.
+moe_status_t launch_quantize_fp8(const void* x, bool x_bf16, int64_t n, float scale, uint8_t* q,
+                                 hipStream_t stream);
+
 // All-to-all dispatch workspace (carved in this order, 256-byte aligned).
 struct A2aLayout {
   size_t pslot, pmask, psorted, perm_ws, total;

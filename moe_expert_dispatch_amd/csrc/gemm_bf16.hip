@@ -405,6 +405,11 @@ __device__ __forceinline__ void lds_read16(bf16x8_t& d, uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF));
 }
 
+template <int OFF>
+__device__ __forceinline__ void lds_read16(int32x4_t& d, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF));
+}
+
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
@@ -420,13 +425,22 @@ struct WItem {
   int rows, row0, col0;
   __amdgpu_buffer_rsrc_t ra, rb, rc;
   uint32_t a_off[4], b_off[4];
+  float sc;  // FP8: input scale times the slot's weight scale
 };
 
-template <int OP, bool GATHER>
+typedef int int32x8_t __attribute__((ext_vector_type(8)));
+typedef int int32x2_t __attribute__((ext_vector_type(2)));
+
+// FP8 (E4M3) operands: a 128-wide K-slice is the same 128 bytes per row as a
+// 64-wide bf16 slice, so stages, DMA and swizzle are shared; a slice is two
+// k-blocks of v_mfma_f32_32x32x64_f8f6f4, each lane holding 32 bytes (two
+// 16-byte chunks) of a row.
+template <int OP, bool GATHER, bool FP8>
 __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma_kernel(
     const uint4* __restrict__ A, const int32_t* __restrict__ offsets, int S,
-    const uint4* __restrict__ W, int N, int Kd, uint16_t* __restrict__ C,
-    const int32_t* __restrict__ gather, int topk, int a_rows) {
+    const uint4* __restrict__ W, int N, int Kd, void* __restrict__ C,
+    const int32_t* __restrict__ gather, int topk, int a_rows, float a_scale,
+    const float* __restrict__ w_scale, float out_inv) {
   __shared__ uint4 smem[2 * WSTAGE_VEC];
   __shared__ int32_t tp[MOE_MAX_SLOTS + 1];
   __shared__ int32_t scan_scratch[NTHR8];
@@ -442,8 +456,10 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma_kernel(
   const int CT = ceil_div(N, BN);
   const int GN = CT < 8 ? CT : 8;
   const int GM = XCD_ITEMS / GN;
-  const int nd = Kd / WBK;  // K-slices
-  const uint32_t row_bytes = (uint32_t)Kd * 2u;
+  constexpr int EB = FP8 ? 1 : 2;                       // operand bytes (A and W are uint4*)
+  constexpr uint32_t OB = (FP8 && OP == 0) ? 1u : 2u;   // output bytes
+  const uint32_t row_bytes = (uint32_t)Kd * EB;
+  const int nd = (int)(row_bytes / (WBK * 2));  // K-slices of 128 bytes per row
 
   build_tile_prefix<NTHR8>(offsets, S, tp, scan_scratch);
   const int RT = uniform(tp[S]);
@@ -457,11 +473,17 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma_kernel(
   uint32_t a_lane[4], b_lane[4];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    a_lane[kb] = (uint32_t)wswz(a_row0, 2 * kb + (lane >> 5)) * 16u;
-    b_lane[kb] = WA_VEC * 16u + (uint32_t)wswz(b_row0, 2 * kb + (lane >> 5)) * 16u;
+    // bf16: the chunk of K-16 block kb. FP8 (kb < 2): the first of the two
+    // chunks of K-64 block kb; the second is chunk ^ 1, i.e. offset ^ 16.
+    const int ch = FP8 ? 4 * kb + 2 * (lane >> 5) : 2 * kb + (lane >> 5);
+    a_lane[kb] = (uint32_t)wswz(a_row0, ch) * 16u;
+    b_lane[kb] = WA_VEC * 16u + (uint32_t)wswz(b_row0, ch) * 16u;
   }
   const uint32_t smem_base = lds_addr(smem);
 
+  // FP8 gather: the pair indices through a buffer resource (sorted rows only)
+  const __amdgpu_buffer_rsrc_t g_rsrc =
+      make_rsrc(gather, GATHER ? (uint32_t)a_rows * (uint32_t)topk * 4u : 0u);
   auto next_item = [&](int w, int* rt, int* ct) {
     while (w < total && !item_tile(w, RT, CT, GM, GN, rt, ct)) w += G;
     return w;
@@ -474,15 +496,21 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma_kernel(
     if constexpr (GATHER)
       x.ra = make_rsrc(A, (uint32_t)a_rows * row_bytes);
     else
-      x.ra = make_rsrc(A + (size_t)x.row0 * (Kd / 8), (uint32_t)x.rows * row_bytes);
-    x.rb = make_rsrc(W + (size_t)s * w_rows * (Kd / 8), (uint32_t)w_rows * row_bytes);
-    x.rc = make_rsrc(C + (size_t)x.row0 * N, (uint32_t)x.rows * (uint32_t)N * 2u);
+      x.ra = make_rsrc(A + (size_t)x.row0 * (Kd / (16 / EB)), (uint32_t)x.rows * row_bytes);
+    x.rb = make_rsrc(W + (size_t)s * w_rows * (Kd / (16 / EB)), (uint32_t)w_rows * row_bytes);
+    x.rc = make_rsrc(static_cast<char*>(C) + (size_t)x.row0 * N * OB,
+                     (uint32_t)x.rows * (uint32_t)N * OB);
+    if constexpr (FP8) x.sc = a_scale * w_scale[s];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int q = wave * 4 + i;  // 8-row block of the stage
       const int r = q * 8 + (lane >> 3);
       const int ch = (lane & 7) ^ ((r >> 1) & 7);
-      if constexpr (GATHER)  // pair index for now; gather_offsets() finishes it
+      if constexpr (GATHER && FP8)  // pair index via a 32-bit offset (no pointer pairs)
+        x.a_off[i] = r < x.rows ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                                      g_rsrc, (uint32_t)(x.row0 + r) * 4u, 0, 0)
+                                : kOOB;
+      else if constexpr (GATHER)  // pair index for now; gather_offsets() finishes it
         x.a_off[i] = r < x.rows ? (uint32_t)gather[x.row0 + r] : kOOB;
       else
         x.a_off[i] = (uint32_t)r * row_bytes + (uint32_t)ch * 16u;
@@ -494,7 +522,10 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma_kernel(
         j = x.col0 + r;
         wrow = j;
       }
-      x.b_off[i] = j < N ? (uint32_t)wrow * row_bytes + (uint32_t)ch * 16u : kOOB;
+      uint32_t cb = (uint32_t)ch * 16u;
+      // FP8: recomputed per item rather than held in registers across the loop
+      if constexpr (FP8) asm volatile("" : "+v"(cb));
+      x.b_off[i] = j < N ? (uint32_t)wrow * row_bytes + cb : kOOB;
     }
   };
   // Pair index -> byte offset of its token's row (the index loads were issued
@@ -574,6 +605,17 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma_kernel(
         int32x4_t{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]}, x.rc,
         col < N ? (r * (uint32_t)N + (uint32_t)col) * 2u : kOOB, 0, 0);
   };
+  // FP8 output: 4 + 4 codes per lane exchanged like store8, one 8-byte store.
+  auto store8q = [&](const WItem& x, uint32_t r, int col, const float* lo, const float* hi) {
+    const uint32_t xq = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+        lo[2], lo[3], __builtin_amdgcn_cvt_pk_fp8_f32(lo[0], lo[1], 0, false), true);
+    const uint32_t yq = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+        hi[2], hi[3], __builtin_amdgcn_cvt_pk_fp8_f32(hi[0], hi[1], 0, false), true);
+    const auto q = __builtin_amdgcn_permlane32_swap(xq, yq, false, false);
+    __builtin_amdgcn_raw_buffer_store_b64(
+        int32x2_t{(int)q[0], (int)q[1]}, x.rc,
+        col < N ? r * (uint32_t)N + (uint32_t)col : kOOB, 0, 0);
+  };
   auto epilogue = [&](const WItem& x) {
     const int ch = 8 * (lane >> 5);
 #pragma unroll
@@ -585,17 +627,29 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma_kernel(
           float o[8];
 #pragma unroll
           for (int v = 0; v < 8; ++v) {
-            const float gt = acc[0][i][4 * g + v];
-            const float up = acc[1][i][4 * g + v];
+            float gt = acc[0][i][4 * g + v];
+            float up = acc[1][i][4 * g + v];
+            if constexpr (FP8) {
+              gt *= x.sc;
+              up *= x.sc;
+            }
             o[v] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;  // silu(g) * u
+            if constexpr (FP8)  // quantized with the output scale, clamped to +-448
+              o[v] = fminf(fmaxf(o[v] * out_inv, -448.0f), 448.0f);
           }
-          store8(x, r, x.col0 + wn * 32 + 8 * g + ch, o, o + 4);
+          if constexpr (FP8)
+            store8q(x, r, x.col0 + wn * 32 + 8 * g + ch, o, o + 4);
+          else
+            store8(x, r, x.col0 + wn * 32 + 8 * g + ch, o, o + 4);
         } else {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             float o[8];
 #pragma unroll
-            for (int v = 0; v < 8; ++v) o[v] = acc[j][i][4 * g + v];
+            for (int v = 0; v < 8; ++v) {
+              o[v] = acc[j][i][4 * g + v];
+              if constexpr (FP8) o[v] *= x.sc;
+            }
             store8(x, r, x.col0 + wn * 64 + j * 32 + 8 * g + ch, o, o + 4);
           }
         }
@@ -647,6 +701,102 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma_kernel(
     }
   };
 
+  // FP8 fragments of one K-64 block, each reloaded right after its last use
+  // (double buffering them would not fit the registers). MFMA x (0..7) of a
+  // block uses weight fragment j = x >> 2 and row fragment i = x & 3. The
+  // next block's fragments are read in the order B0 (after MFMA 3), A0 (after
+  // 4), A1 (5), A2 (6), A3 and B1 (7), two 16-byte reads each, so before MFMA
+  // x the reads allowed outstanding are 8, 6, 4, 2 for x = 0..3 and 2 (the
+  // next block's B0) for x = 4.
+  int32x8_t ga[4], gb[2];
+  // the two 16-byte halves of a fragment, read into one 8-register tuple
+  auto rd32 = [&](int32x8_t& f, uint32_t a0, uint32_t a1, auto offc) {
+    constexpr int off = decltype(offc)::value;
+    int32x4_t lo, hi;
+    lds_read16<off>(lo, a0);
+    lds_read16<off>(hi, a1);
+    f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto rdf = [&](int f, auto kbc, uint32_t base) {
+    constexpr int kb = decltype(kbc)::value;
+    const uint32_t a0 = base + a_lane[kb], a1 = base + (a_lane[kb] ^ 16u);
+    const uint32_t b0 = base + b_lane[kb], b1 = base + (b_lane[kb] ^ 16u);
+    switch (f) {
+      case 0: rd32(ga[0], a0, a1, std::integral_constant<int, 0 * 4096>{}); break;
+      case 1: rd32(ga[1], a0, a1, std::integral_constant<int, 1 * 4096>{}); break;
+      case 2: rd32(ga[2], a0, a1, std::integral_constant<int, 2 * 4096>{}); break;
+      case 3: rd32(ga[3], a0, a1, std::integral_constant<int, 3 * 4096>{}); break;
+      case 4: rd32(gb[0], b0, b1, std::integral_constant<int, bfragw_off<OP>(0)>{}); break;
+      default: rd32(gb[1], b0, b1, std::integral_constant<int, bfragw_off<OP>(1)>{}); break;
+    }
+  };
+  auto wfr = [&](int x, bool last) {  // wait for the fragments MFMA x needs first
+    switch (x) {
+      case 0: asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(gb[0]), "+v"(ga[0])); break;
+      case 1: asm volatile("s_waitcnt lgkmcnt(6)" : "+v"(ga[1])); break;
+      case 2: asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(ga[2])); break;
+      case 3: asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(ga[3])); break;
+      default:
+        if (last)
+          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(gb[1]));
+        else
+          asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(gb[1]));
+        break;
+    }
+  };
+  auto wait_all8 = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(ga[0]), "+v"(ga[1]), "+v"(ga[2]), "+v"(ga[3]), "+v"(gb[0]), "+v"(gb[1]));
+  };
+  auto mf8 = [&](int x, auto first) {
+    const int j = x >> 2, i = x & 3;
+    if constexpr (decltype(first)::value)
+      acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(gb[j], ga[i], floatx16{}, 0, 0, 0,
+                                                                  0, 0, 0);
+    else
+      acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(gb[j], ga[i], acc[j][i], 0, 0, 0,
+                                                                  0, 0, 0);
+  };
+  // K-64 block kb of slice d. Block 0 reloads block 1 from the same stage.
+  // Block 1 first waits for its last fragments, for this wave's DMA of slice
+  // d+1 and at the workgroup barrier (after which slice d+1 is complete and
+  // stage d & 1 is read by no one); then it reloads block 0 of slice d+1
+  // from the other stage and issues the DMA of slice d+2 into stage d & 1,
+  // two instructions after each of its last four MFMAs. In the item's last
+  // slice (`last`), block 1 reloads and moves nothing.
+  auto kblock = [&](int d, auto kbc, auto first, auto lastc) {
+    constexpr int kb = decltype(kbc)::value;
+    constexpr bool tail = kb == 1 && decltype(lastc)::value;
+    const uint32_t base = smem_base + (uint32_t)(d & 1) * WSTAGE_BYTES;
+    const uint32_t rb = kb == 0 ? base : smem_base + (uint32_t)((d + 1) & 1) * WSTAGE_BYTES;
+    const std::integral_constant<int, kb == 0 ? 1 : 0> rk;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      if (x < 4) wfr(x, false);
+      if (x == 4) {
+        if constexpr (kb == 1) {
+          wfr(4, true);
+          vm_wait<0>();
+          __builtin_amdgcn_s_barrier();
+          if constexpr (!tail) rdf(4, rk, rb);
+        } else {
+          wfr(4, false);
+        }
+      }
+      mf8(x, first);  // each accumulator is written by one MFMA per block
+      if (kb == 0 && x == 3) rdf(4, rk, rb);
+      if (!tail && x >= 4) rdf(x - 4, rk, rb);
+      if (!tail && x == 7) rdf(5, rk, rb);
+      if constexpr (kb == 1 && !tail) {
+        if (x >= 4) {
+          dma(cur, 2 * (x - 4), d + 2);
+          dma(cur, 2 * (x - 4) + 1, d + 2);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   // A slice for waves whose rows are all padding (the lower 128 rows of an
   // item with at most 128 rows): only their share of the operand DMAs and
   // the barrier, no fragment reads or MFMAs.
@@ -686,18 +836,48 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma_kernel(
     // The epilogue sits inside the computing branch, so the accumulators are
     // not live across the pass-only slices.
     if (!skip) {
+      if constexpr (FP8) {
+        const std::integral_constant<int, 0> k0;
+        const std::integral_constant<int, 1> k1;
+        // block 0 of slice 0, in the order the waits assume
+        rdf(4, k0, smem_base);
 #pragma unroll
-      for (int x = 0; x < 6; ++x) read8(x, f0a, f0b, smem_base + a_lane[0], smem_base + b_lane[0]);
-      dstep(0, std::true_type{});
-      for (int d = 1; d < dlast; ++d) dstep(d, std::false_type{});
-      if constexpr (GATHER) {
-        next_setup();
-        dstep(nd - 1, std::false_type{});
+        for (int f = 0; f < 4; ++f) rdf(f, k0, smem_base);
+        rdf(5, k0, smem_base);
+        const std::false_type no;
+        kblock(0, k0, std::true_type{}, no);
+        kblock(0, k1, no, no);
+        for (int d = 1; d < nd - 1; ++d) {
+          kblock(d, k0, no, no);
+          kblock(d, k1, no, no);
+        }
+        kblock(nd - 1, k0, no, no);
+        kblock(nd - 1, k1, no, std::true_type{});
+        vm_wait<0>();
+        wait_all8();
+      } else {
+#pragma unroll
+        for (int x = 0; x < 6; ++x)
+          read8(x, f0a, f0b, smem_base + a_lane[0], smem_base + b_lane[0]);
+        dstep(0, std::true_type{});
+        for (int d = 1; d < dlast; ++d) dstep(d, std::false_type{});
+        if constexpr (GATHER) {
+          next_setup();
+          dstep(nd - 1, std::false_type{});
+        }
+        vm_wait<0>();
+        wait_frags(f0a, f0b);
       }
-      vm_wait<0>();
-      wait_frags(f0a, f0b);
       __builtin_amdgcn_s_barrier();
-      if constexpr (!GATHER) next_setup();
+      if constexpr (!GATHER) {
+        next_setup();
+      } else if constexpr (FP8) {
+        // FP8 fragments leave no registers for setup inside the K-loop: the
+        // next item is set up here and its index loads drained before any
+        // epilogue store.
+        next_setup();
+        vm_wait<0>();
+      }
       epilogue(done);
     } else {
       for (int d = 0; d < dlast; ++d) pass_step(d);
@@ -751,14 +931,14 @@ moe_status_t launch_gemm_bf16(moe_gemm_op_t op, const void* a, const int32_t* of
   const bool dma = dma_ok(Kd);
   if (op == MOE_GEMM_GATE_UP_SWIGLU) {
     if (dma)
-      grouped_gemm_bf16_dma_kernel<0, false>
-          <<<G, NTHR8, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16, nullptr, 1, 0);
+      grouped_gemm_bf16_dma_kernel<0, false, false><<<G, NTHR8, 0, stream>>>(
+          a4, offsets, S, w4, N, Kd, c16, nullptr, 1, 0, 1.0f, nullptr, 1.0f);
     else
       grouped_gemm_bf16_kernel<0><<<G, NTHR, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
   } else {
     if (dma)
-      grouped_gemm_bf16_dma_kernel<1, false>
-          <<<G, NTHR8, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16, nullptr, 1, 0);
+      grouped_gemm_bf16_dma_kernel<1, false, false><<<G, NTHR8, 0, stream>>>(
+          a4, offsets, S, w4, N, Kd, c16, nullptr, 1, 0, 1.0f, nullptr, 1.0f);
     else
       grouped_gemm_bf16_kernel<1><<<G, NTHR, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
   }
@@ -778,9 +958,52 @@ moe_status_t launch_gemm_bf16_gate_up_gathered(const void* x, int T, int K,
   if (!gemm_bf16_gather_ok(T, H)) return MOE_ERR_UNSUPPORTED;
   if (max_rows == 0) return MOE_OK;
   const int G = gemm_grid(max_rows, S, I, BROWS / 2);
-  grouped_gemm_bf16_dma_kernel<0, true><<<G, NTHR8, 0, stream>>>(
-      static_cast<const uint4*>(x), offsets, S, static_cast<const uint4*>(w), I, H,
-      static_cast<uint16_t*>(c), sorted_pairs, K, T);
+  grouped_gemm_bf16_dma_kernel<0, true, false><<<G, NTHR8, 0, stream>>>(
+      static_cast<const uint4*>(x), offsets, S, static_cast<const uint4*>(w), I, H, c,
+      sorted_pairs, K, T, 1.0f, nullptr, 1.0f);
+  return launch_status();
+}
+
+// ---------------------------------------------------------------- FP8
+bool gemm_fp8_ok(int Kd) { return Kd % (2 * WBK) == 0 && Kd >= 4 * WBK; }
+
+bool gemm_fp8_gather_ok(int T, int H) {
+  return gemm_fp8_ok(H) && (size_t)T * (size_t)H < (size_t)kOOB;
+}
+
+moe_status_t launch_gemm_fp8(moe_gemm_op_t op, const uint8_t* a, float a_scale,
+                             const int32_t* offsets, int S, int max_rows, const uint8_t* w,
+                             const float* w_scale, int H, int I, void* c, float out_scale,
+                             hipStream_t stream) {
+  const bool gu = op == MOE_GEMM_GATE_UP_SWIGLU;
+  const int N = gu ? I : H;
+  const int Kd = gu ? H : I;
+  if (!gemm_fp8_ok(Kd)) return MOE_ERR_UNSUPPORTED;
+  if (max_rows == 0) return MOE_OK;
+  const int G = gemm_grid(max_rows, S, N, gu ? BROWS / 2 : BROWS);
+  const uint4* a4 = reinterpret_cast<const uint4*>(a);
+  const uint4* w4 = reinterpret_cast<const uint4*>(w);
+  if (gu)
+    grouped_gemm_bf16_dma_kernel<0, false, true><<<G, NTHR8, 0, stream>>>(
+        a4, offsets, S, w4, N, Kd, c, nullptr, 1, 0, a_scale, w_scale, 1.0f / out_scale);
+  else
+    grouped_gemm_bf16_dma_kernel<1, false, true><<<G, NTHR8, 0, stream>>>(
+        a4, offsets, S, w4, N, Kd, c, nullptr, 1, 0, a_scale, w_scale, 1.0f);
+  return launch_status();
+}
+
+moe_status_t launch_gemm_fp8_gate_up_gathered(const uint8_t* xq, int T, int K,
+                                              const int32_t* sorted_pairs,
+                                              const int32_t* offsets, int S, int max_rows,
+                                              const uint8_t* w, const float* w_scale,
+                                              float a_scale, int H, int I, void* c,
+                                              float out_scale, hipStream_t stream) {
+  if (!gemm_fp8_gather_ok(T, H)) return MOE_ERR_UNSUPPORTED;
+  if (max_rows == 0) return MOE_OK;
+  const int G = gemm_grid(max_rows, S, I, BROWS / 2);
+  grouped_gemm_bf16_dma_kernel<0, true, true><<<G, NTHR8, 0, stream>>>(
+      reinterpret_cast<const uint4*>(xq), offsets, S, reinterpret_cast<const uint4*>(w), I, H,
+      c, sorted_pairs, K, T, a_scale, w_scale, 1.0f / out_scale);
   return launch_status();
 }
 

@@ -34,7 +34,10 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool dtype_ok(moe_dtype_t dt) { return dt == MOE_DTYPE_F32 || dt == MOE_DTYPE_BF16; }
-int dtype_bytes(moe_dtype_t dt) { return dt == MOE_DTYPE_F32 ? 4 : 2; }
+int dtype_bytes(moe_dtype_t dt) {
+  return dt == MOE_DTYPE_F32 ? 4 : dt == MOE_DTYPE_FP8_E4M3 ? 1 : 2;
+}
+bool scale_ok(float s) { return s > 0.0f && s <= 3.4e38f; }  // finite, positive (false for NaN)
 
 // T * K and T * K * max(H, I) must stay addressable with 32-bit row indices.
 bool pairs_fit(int T, int K) { return (long long)T * K < (1LL << 31); }
@@ -118,14 +121,16 @@ moe_status_t launch_gemm(moe_gemm_op_t op, moe_dtype_t dt, const void* a, const 
 
 // Workspace of moe_forward, carved in this order (each 256-byte aligned).
 struct ForwardLayout {
-  size_t ids, w, slot, w_masked, mask, offsets, sorted_pairs, pair_row, perm_ws, x_perm, act;
+  size_t ids, w, slot, w_masked, mask, offsets, sorted_pairs, pair_row, perm_ws, x_perm, act, xq;
   size_t total;
 };
 
 ForwardLayout forward_layout(const moe_config_t* c) {
   ForwardLayout L;
   const size_t P = (size_t)c->T_max * c->K;
+  const bool fp8 = c->dtype == MOE_DTYPE_FP8_E4M3;
   const size_t eb = dtype_bytes(c->dtype);
+  const size_t yb = fp8 ? 2 : eb;  // FP8: the expert outputs are bf16
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -141,8 +146,9 @@ ForwardLayout forward_layout(const moe_config_t* c) {
   L.sorted_pairs = take(P * 4);
   L.pair_row = take(P * 4);
   L.perm_ws = take(permute_plan(c->T_max, c->K, c->S).ws_bytes);
-  L.x_perm = take(P * c->H * eb);  // later reused for the down-projection output
+  L.x_perm = take(P * c->H * yb);  // later reused for the down-projection output
   L.act = take(P * c->I * eb);
+  L.xq = take(fp8 ? (size_t)c->T_max * c->H : 0);  // FP8: the quantized input
   L.total = off;
   return L;
 }
@@ -185,7 +191,12 @@ moe_status_t check_config(const moe_config_t* c) {
       c->ep_rank >= c->ep_size)
     return MOE_ERR_INVALID_ARG;
   if (c->S < c->E_global / c->ep_size) return MOE_ERR_INVALID_ARG;
-  if (!dtype_ok(c->dtype) || !dtype_ok(c->out_dtype)) return MOE_ERR_UNSUPPORTED;
+  const bool fp8 = c->dtype == MOE_DTYPE_FP8_E4M3;
+  if ((!dtype_ok(c->dtype) && !fp8) || !dtype_ok(c->out_dtype)) return MOE_ERR_UNSUPPORTED;
+  if (fp8 && (!scale_ok(c->a1_scale) || !scale_ok(c->a2_scale))) return MOE_ERR_INVALID_ARG;
+  if (fp8 && (c->routing_on_input || !gemm_fp8_ok(c->H) || !gemm_fp8_ok(c->I) ||
+              !gemm_fp8_gather_ok(c->T_max, c->H)))
+    return MOE_ERR_UNSUPPORTED;
   if (c->E_global > MOE_MAX_EXPERTS || c->K > MOE_MAX_TOPK || c->S > MOE_MAX_SLOTS)
     return MOE_ERR_UNSUPPORTED;
   if (c->H % 8 != 0 || c->I % 8 != 0 || !pairs_fit(c->T_max, c->K)) return MOE_ERR_UNSUPPORTED;
@@ -325,6 +336,8 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_forward_args_t* args
         !aligned16(args->out))
       return MOE_ERR_INVALID_ARG;
     if (args->shared_out && !aligned16(args->shared_out)) return MOE_ERR_INVALID_ARG;
+    if (cfg->dtype == MOE_DTYPE_FP8_E4M3 && (!args->w_gate_up_scale || !args->w_down_scale))
+      return MOE_ERR_INVALID_ARG;
   }
   const ForwardLayout L = forward_layout(cfg);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
@@ -342,7 +355,9 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_forward_args_t* args
   void* perm_ws = base + L.perm_ws;
   void* x_perm = base + L.x_perm;
   void* act = base + L.act;
+  uint8_t* xq = reinterpret_cast<uint8_t*>(base + L.xq);
   void* y = x_perm;  // grouped GEMM 1 has consumed x_perm when GEMM 2 writes
+  const bool fp8 = cfg->dtype == MOE_DTYPE_FP8_E4M3;
 
   auto mark = [&](int ev) -> moe_status_t {
     if (args->events[ev] && hipEventRecord(args->events[ev], stream) != hipSuccess)
@@ -371,28 +386,63 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_forward_args_t* args
   // itself, so the permutation only orders the pairs (no x_perm copy).
   // Input-side routing gathers rows scaled by the pair weight instead.
   const bool on_input = cfg->routing_on_input != 0;
+  // FP8: x is quantized once per token and GEMM 1 gathers the code rows.
   const bool fused_gather =
-      !on_input && cfg->dtype == MOE_DTYPE_BF16 && gemm_bf16_gather_ok(T, H);
-  MOE_TRY(launch_permute(args->x, dtype_bytes(cfg->dtype), T, H, K, slot, mask, S, offsets,
-                         sorted_pairs, pair_row, fused_gather ? nullptr : x_perm, perm_ws,
-                         stream, 0, on_input ? w_masked : nullptr));
+      fp8 || (!on_input && cfg->dtype == MOE_DTYPE_BF16 && gemm_bf16_gather_ok(T, H));
+  if (fp8) MOE_TRY(launch_quantize_fp8(args->x, true, (int64_t)T * H, cfg->a1_scale, xq, stream));
+  MOE_TRY(launch_permute(args->x, fp8 ? 2 : dtype_bytes(cfg->dtype), T, H, K, slot, mask, S,
+                         offsets, sorted_pairs, pair_row, fused_gather ? nullptr : x_perm,
+                         perm_ws, stream, 0, on_input ? w_masked : nullptr));
   MOE_TRY(mark(MOE_EV_PERMUTED));
-  if (fused_gather)
+  if (fp8)
+    MOE_TRY(launch_gemm_fp8_gate_up_gathered(
+        xq, T, K, sorted_pairs, offsets, S, T * K, static_cast<const uint8_t*>(args->w_gate_up),
+        args->w_gate_up_scale, cfg->a1_scale, H, I, act, cfg->a2_scale, stream));
+  else if (fused_gather)
     MOE_TRY(launch_gemm_bf16_gate_up_gathered(args->x, T, K, sorted_pairs, offsets, S, T * K,
                                               args->w_gate_up, H, I, act, stream));
   else
     MOE_TRY(launch_gemm(MOE_GEMM_GATE_UP_SWIGLU, cfg->dtype, x_perm, offsets, S, T * K,
                         args->w_gate_up, H, I, act, stream));
   MOE_TRY(mark(MOE_EV_GATE_UP));
-  MOE_TRY(launch_gemm(MOE_GEMM_DOWN, cfg->dtype, act, offsets, S, T * K, args->w_down, H, I, y,
-                      stream));
+  if (fp8)
+    MOE_TRY(launch_gemm_fp8(MOE_GEMM_DOWN, static_cast<const uint8_t*>(act), cfg->a2_scale,
+                            offsets, S, T * K, static_cast<const uint8_t*>(args->w_down),
+                            args->w_down_scale, H, I, y, 1.0f, stream));
+  else
+    MOE_TRY(launch_gemm(MOE_GEMM_DOWN, cfg->dtype, act, offsets, S, T * K, args->w_down, H, I,
+                        y, stream));
   MOE_TRY(mark(MOE_EV_DOWN));
-  MOE_TRY(launch_combine(y, cfg->dtype, pair_row, on_input ? nullptr : w_masked, T, K, H,
-                         args->out, cfg->out_dtype, cfg->accumulate, stream, args->shared_out,
-                         cfg->dtype));
+  const moe_dtype_t ydt = fp8 ? MOE_DTYPE_BF16 : cfg->dtype;
+  MOE_TRY(launch_combine(y, ydt, pair_row, on_input ? nullptr : w_masked, T, K, H, args->out,
+                         cfg->out_dtype, cfg->accumulate, stream, args->shared_out, ydt));
   MOE_TRY(mark(MOE_EV_COMBINED));
 #undef MOE_TRY
   return MOE_OK;
+}
+
+moe_status_t moe_quantize_fp8(const void* x, moe_dtype_t x_dt, int64_t n, float scale,
+                              uint8_t* q, hipStream_t stream) {
+  if (n < 0 || !scale_ok(scale)) return MOE_ERR_INVALID_ARG;
+  if (x_dt != MOE_DTYPE_BF16 && x_dt != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
+  if (n == 0) return MOE_OK;
+  if (!x || !q || !aligned16(x) || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  return launch_quantize_fp8(x, x_dt == MOE_DTYPE_BF16, n, scale, q, stream);
+}
+
+moe_status_t moe_grouped_gemm_fp8(moe_gemm_op_t op, const uint8_t* a, float a_scale,
+                                  const int32_t* offsets, int S, int max_rows, const uint8_t* w,
+                                  const float* w_scale, int H, int I, void* c, float c_scale,
+                                  hipStream_t stream) {
+  // the shape, pointer and alignment rules of moe_grouped_gemm
+  const moe_status_t st = check_gemm(op, MOE_DTYPE_BF16, a, offsets, S, max_rows, w, H, I, c);
+  if (st != MOE_OK) return st;
+  if (!scale_ok(a_scale) || (op == MOE_GEMM_GATE_UP_SWIGLU && !scale_ok(c_scale)))
+    return MOE_ERR_INVALID_ARG;
+  if (max_rows > 0 && !w_scale) return MOE_ERR_INVALID_ARG;
+  if (!gemm_fp8_ok(op == MOE_GEMM_GATE_UP_SWIGLU ? H : I)) return MOE_ERR_UNSUPPORTED;
+  return launch_gemm_fp8(op, a, a_scale, offsets, S, max_rows, w, w_scale, H, I, c, c_scale,
+                         stream);
 }
 
 size_t moe_a2a_dispatch_workspace_size(int T, int ep_size, int cap) {

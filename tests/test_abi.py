@@ -206,3 +206,61 @@ def test_python_layer_rejects_host_tensors():
     import torch
     with pytest.raises(ValueError):
         moe.route(torch.zeros(4, 8), 2, True)
+
+
+def test_quantize_fp8_validation(so):
+    f = so.moe_quantize_fp8
+    fake = ctypes.c_void_p(256)
+    assert f(fake, 1, -1, 1.0, fake, None) == INVALID                  # n < 0
+    assert f(fake, 1, 16, 0.0, fake, None) == INVALID                  # scale <= 0
+    assert f(fake, 1, 16, float("nan"), fake, None) == INVALID
+    assert f(fake, 1, 16, float("inf"), fake, None) == INVALID
+    assert f(fake, 2, 16, 1.0, fake, None) == UNSUPPORTED              # fp8 input
+    assert f(None, 1, 16, 1.0, fake, None) == INVALID                  # null x
+    assert f(fake, 1, 16, 1.0, ctypes.c_void_p(264), None) == INVALID  # misaligned q
+    assert f(None, 1, 0, 1.0, None, None) == 0                         # empty: no work
+
+
+def test_grouped_gemm_fp8_validation(so):
+    f = so.moe_grouped_gemm_fp8
+    fake = ctypes.c_void_p(256)
+
+    def call(op=0, a_scale=1.0, S=4, rows=16, H=256, I=256, c_scale=1.0, w_scale=fake, a=fake):
+        return f(op, a, a_scale, fake, S, rows, fake, w_scale, H, I, fake, c_scale, None)
+
+    assert call(op=5) == INVALID
+    assert call(a_scale=0.0) == INVALID
+    assert call(c_scale=-1.0) == INVALID              # gate/up output scale
+    assert call(w_scale=None) == INVALID
+    assert call(a=None) == INVALID
+    assert call(H=192) == UNSUPPORTED                 # gate/up contraction not a multiple of 128
+    assert call(H=128) == UNSUPPORTED                 # one 128-wide slice only
+    assert call(op=1, I=320) == UNSUPPORTED           # down contraction is I
+    # zero rows: validation passes and nothing is launched; down ignores c_scale
+    assert call(op=1, c_scale=0.0, H=64, rows=0) == 0
+    assert call(op=0, c_scale=0.0, rows=0) == INVALID
+
+
+def test_forward_fp8_config_validation(so):
+    import torch
+    ok = _cfg(H=256, I=256, dtype=moe.FP8, a1_scale=0.5, a2_scale=0.25)
+    n = so.moe_forward_workspace_size(ctypes.byref(ok.c_struct()))
+    P = 16 * 2
+    # bf16 expert outputs, fp8 activations and the quantized input
+    assert n >= P * 256 * 2 + P * 256 + 16 * 256
+    assert ok.out_dtype == torch.bfloat16
+    bad = [_cfg(H=192, I=256, dtype=moe.FP8),              # H % 128
+           _cfg(H=256, I=128, dtype=moe.FP8),              # I < 256
+           _cfg(H=256, I=256, dtype=moe.FP8, a1_scale=0.0),
+           _cfg(H=256, I=256, dtype=moe.FP8, a2_scale=float("nan")),
+           _cfg(H=256, I=256, dtype=moe.FP8, routing_on_input=True),
+           _cfg(H=256, I=256, dtype=moe.FP8, out_dtype=moe.FP8)]
+    for b in bad:
+        assert so.moe_forward_workspace_size(ctypes.byref(b.c_struct())) == 0
+    # missing weight scales are rejected before any launch
+    args = moe._ForwardArgs()
+    for name in ("x", "logits", "w_gate_up", "w_down", "out"):
+        setattr(args, name, 256)
+    st = so.moe_forward(ctypes.byref(ok.c_struct()), ctypes.byref(args), ctypes.c_void_p(256),
+                        n, None)
+    assert st == INVALID

@@ -32,7 +32,7 @@ class WorkloadConfig:
     E: int          # global routed experts
     K: int
     renormalize: bool
-    dtype: str      # "f32" or "bf16"
+    dtype: str      # "f32", "bf16" or "fp8" (bf16 input, E4M3 expert weights)
     router: str     # "gauss", "gauss_bias", "zipf"
     ep_size: int = 1
     n_replicated: int = 0     # experts given a second slot (zipf workload)
@@ -43,6 +43,8 @@ class WorkloadConfig:
     topk_group: int = 0        # groups kept
     shared_expert: bool = False     # a shared-expert output [T, H] is added in the combine
     routing_on_input: bool = False  # routing weights applied to the expert input
+    a1_scale: float = 1.0 / 56.0    # fp8: scale of the quantized expert input (x ~ N(0,1))
+    a2_scale: float = 1.0 / 14.0    # fp8: scale of the quantized SwiGLU output
 
     @property
     def E_local(self) -> int:
@@ -84,6 +86,11 @@ CONFIGS = {
         WorkloadConfig("deepseek_v2_grouped_bf16", T=8192, H=5120, I=1536, E=160, K=6,
                        renormalize=True, dtype="bf16", router="gauss_bias", bias_std=0.5,
                        num_expert_group=8, topk_group=3),
+        # FP8 (E4M3) expert weights and activations on the two largest shapes
+        WorkloadConfig("redundant_slots_zipf_fp8", T=16384, H=4096, I=1024, E=64, K=8,
+                       renormalize=True, dtype="fp8", router="zipf", n_replicated=16),
+        WorkloadConfig("deepseek_v2_fp8", T=8192, H=5120, I=1536, E=160, K=6,
+                       renormalize=True, dtype="fp8", router="gauss_bias", bias_std=0.5),
     ]
 }
 

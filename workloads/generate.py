@@ -17,6 +17,12 @@ cast to bf16 with round-to-nearest-even where the workload is bf16):
                  down [H, I] ~ N(0, 1/sqrt(I)); stored expert-indexed as
                  w_gate_up [E, 2I, H] (gate rows, then up rows) and
                  w_down [E, H, I].
+  fp8 workloads: x and the router as above (x in bf16); expert weights are
+                 drawn directly as OCP E4M3 codes: sign uniform, magnitude
+                 code uniform over 0x28..0x3f (values 0.25 .. 1.875, rms
+                 0.97), with one scale per expert and matrix, 1/sqrt(H) for
+                 gate/up and 1/sqrt(I) for down (dequantized std about
+                 0.97/sqrt(fan-in), close to the bf16 recipe).
 Every tensor draws from its own sub-generator whose seed is derived from
 (seed, tensor name, expert index) by SHA-256, so experts can be drawn in
 parallel and any subset is reproducible on its own.
@@ -34,7 +40,7 @@ import torch
 
 from .configs import WorkloadConfig
 
-_TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+_TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.bfloat16}  # fp8: x
 
 
 def _sub_seed(seed: int, tag: str, idx: int = 0) -> int:
@@ -59,12 +65,20 @@ class MoEInputs:
     w_gate_up: torch.Tensor         # [E, 2I, H] cfg.dtype, expert-indexed
     w_down: torch.Tensor            # [E, H, I] cfg.dtype, expert-indexed
     popularity_rank: Optional[torch.Tensor] = None  # [E] int64 (zipf router)
+    w_gate_up_scale: Optional[torch.Tensor] = None  # fp8: [E] f32
+    w_down_scale: Optional[torch.Tensor] = None     # fp8: [E] f32
 
     def share_weights(self, ep_rank: int) -> Tuple[torch.Tensor, torch.Tensor]:
         """Expert weights held by one EP rank: experts [r*E_l, (r+1)*E_l)."""
         El = self.cfg.E_local
         lo = ep_rank * El
         return self.w_gate_up[lo:lo + El], self.w_down[lo:lo + El]
+
+    def share_scales(self, ep_rank: int) -> Tuple[torch.Tensor, torch.Tensor]:
+        """fp8: the per-expert weight scales of one EP rank's experts."""
+        El = self.cfg.E_local
+        lo = ep_rank * El
+        return self.w_gate_up_scale[lo:lo + El], self.w_down_scale[lo:lo + El]
 
     def replicated_experts(self) -> List[int]:
         """Experts that get a second slot: the n_replicated most popular ones,
@@ -77,8 +91,20 @@ class MoEInputs:
         return [int(e) for e in order[:n]]
 
 
+def _codes(shape, g: torch.Generator) -> torch.Tensor:
+    """E4M3 codes: random sign bit, magnitude code uniform over 0x28..0x3f."""
+    mag = torch.randint(0x28, 0x40, shape, generator=g, dtype=torch.uint8)
+    sign = torch.randint(0, 2, shape, generator=g, dtype=torch.uint8) << 7
+    return mag | sign
+
+
 def _fill_expert(cfg: WorkloadConfig, e: int, wgu: torch.Tensor, wd: torch.Tensor) -> None:
     H, I = cfg.H, cfg.I
+    if cfg.dtype == "fp8":
+        wgu[e, :I].copy_(_codes((I, H), _gen(cfg.seed, "w_gate", e)))
+        wgu[e, I:].copy_(_codes((I, H), _gen(cfg.seed, "w_up", e)))
+        wd[e].copy_(_codes((H, I), _gen(cfg.seed, "w_down", e)))
+        return
     dt = _TORCH_DT[cfg.dtype]
     g = _gen(cfg.seed, "w_gate", e)
     wgu[e, :I].copy_((torch.randn(I, H, generator=g) * (1.0 / math.sqrt(H))).to(dt))
@@ -92,7 +118,7 @@ def make_expert_weights(cfg: WorkloadConfig, experts: Optional[Sequence[int]] = 
                         threads: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Expert weights [E, 2I, H] and [E, H, I]; only `experts` are drawn if given
     (the others are left zero)."""
-    dt = _TORCH_DT[cfg.dtype]
+    dt = torch.uint8 if cfg.dtype == "fp8" else _TORCH_DT[cfg.dtype]
     wgu = torch.empty(cfg.E, 2 * cfg.I, cfg.H, dtype=dt)
     wd = torch.empty(cfg.E, cfg.H, cfg.I, dtype=dt)
     if experts is not None:
@@ -144,7 +170,11 @@ def make_inputs(cfg: WorkloadConfig, with_weights: bool = True,
     else:
         wgu = torch.empty(0, dtype=dt)
         wd = torch.empty(0, dtype=dt)
-    return MoEInputs(cfg, x, logits, wgu, wd, rank)
+    inp = MoEInputs(cfg, x, logits, wgu, wd, rank)
+    if cfg.dtype == "fp8":
+        inp.w_gate_up_scale = torch.full((cfg.E,), 1.0 / math.sqrt(cfg.H), dtype=torch.float32)
+        inp.w_down_scale = torch.full((cfg.E,), 1.0 / math.sqrt(cfg.I), dtype=torch.float32)
+    return inp
 
 
 def identity_slot_table(E_local: int) -> Tuple[torch.Tensor, torch.Tensor]:
