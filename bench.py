@@ -34,7 +34,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_F32_TFLOPS = 157.3  # MI355X fp32 vector (FMA) peak
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_traffic.json")
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")  # <workload>_gate_up_traffic.json
 GEMM_SRC = os.path.join(ROOT, "moe_expert_dispatch_amd", "csrc", "gemm_bf16.hip")
 
 
@@ -143,7 +143,7 @@ def gemm_traffic(workload):
     None if the kernel source changed since the counters were taken or they
     were taken on another workload."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(TRAFFIC_DIR, f"{workload}_gate_up_traffic.json")) as f:
             rec = json.load(f)
         with open(GEMM_SRC, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
@@ -318,7 +318,7 @@ def main():
                   + 2 * P_in * cfg.I * wb + P_in * cfg.H * eb)
     gemm_floor_ms = max((fl_gu + fl_dn) / (peak_tf * 1e9), gemm_bytes / (PEAK_HBM_GBPS * 1e6))
     gemm_ms = stage_ms["gemm_gate_up"] + stage_ms["gemm_down"]
-    traffic = gemm_traffic(cfg.name) if cfg.dtype == "bf16" else None
+    traffic = gemm_traffic(cfg.name) if cfg.dtype in ("bf16", "fp8") else None
 
     res = {
         "metric": METRIC,
@@ -343,7 +343,7 @@ def main():
                      if cfg.dtype == "bf16" else
                      {"bound": "mfma", "kernel": "grouped_gemm fp8 (E4M3) gate/up + SwiGLU",
                       "achieved": gu_tflops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                      "frac": gu_tflops / PEAK_FP8_TFLOPS, "traffic": None}
+                      "frac": gu_tflops / PEAK_FP8_TFLOPS, "traffic": traffic}
                      if fp8 else
                      {"bound": "alu", "kernel": "grouped_gemm_f32 gate/up + SwiGLU (FMA)",
                       "achieved": gu_tflops, "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
