@@ -35,7 +35,7 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_F32_TFLOPS = 157.3  # MI355X fp32 vector (FMA) peak
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")  # <workload>_gate_up_traffic.json
-GEMM_SRC = os.path.join(ROOT, "moe_expert_dispatch_amd", "csrc", "gemm_bf16.hip")
+GEMM_SRC = os.path.join(ROOT, "moe_expert_dispatch_amd", "csrc", "gemm_mfma.hip")
 
 
 def parse():

@@ -51,7 +51,7 @@ COMPILE_FLAGS = [
 # may appear in it: register spills to scratch would shift every count. The
 # build asks for the resource-usage remarks and rejects such a kernel (file ->
 # kernel-name fragment) if it uses scratch.
-NO_SCRATCH = {"gemm_bf16.hip": "grouped_gemm_bf16_dma_kernel"}
+NO_SCRATCH = {"gemm_mfma.hip": "grouped_gemm_dma_kernel"}
 _REMARK = "kernel-resource-usage"
 
 

@@ -1,9 +1,11 @@
-// Grouped bf16 GEMMs of the expert MLP on gfx950 matrix cores (MFMA).
+// Grouped GEMMs of the expert MLP on gfx950 matrix cores (MFMA): bf16, and
+// FP8 (E4M3) with per-slot scales.
 //
 // Source: TensorRT-LLM PR #10985 review of torch_moe.py (gated MLP with an
-// activation function over stacked per-expert parameters) and vLLM
-// ep_fused_moe_patch.py docstring (per-expert compute that skips experts with
-// no tokens). The gate is SwiGLU, silu(z) = z / (1 + exp(-z)).
+// activation function over stacked per-expert parameters; FP8 variants of the
+// quantized MoE ops) and vLLM ep_fused_moe_patch.py docstring (per-expert
+// compute that skips experts with no tokens). The gate is SwiGLU,
+// silu(z) = z / (1 + exp(-z)).
 //
 // One persistent launch covers every slot. Rows of slot s are the contiguous
 // block a[offsets[s] .. offsets[s+1]) produced by the permutation, so each
@@ -436,7 +438,7 @@ typedef int int32x2_t __attribute__((ext_vector_type(2)));
 // k-blocks of v_mfma_f32_32x32x64_f8f6f4, each lane holding 32 bytes (two
 // 16-byte chunks) of a row.
 template <int OP, bool GATHER, bool FP8>
-__global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_bf16_dma_kernel(
+__global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
     const uint4* __restrict__ A, const int32_t* __restrict__ offsets, int S,
     const uint4* __restrict__ W, int N, int Kd, void* __restrict__ C,
     const int32_t* __restrict__ gather, int topk, int a_rows, float a_scale,
@@ -931,13 +933,13 @@ moe_status_t launch_gemm_bf16(moe_gemm_op_t op, const void* a, const int32_t* of
   const bool dma = dma_ok(Kd);
   if (op == MOE_GEMM_GATE_UP_SWIGLU) {
     if (dma)
-      grouped_gemm_bf16_dma_kernel<0, false, false><<<G, NTHR8, 0, stream>>>(
+      grouped_gemm_dma_kernel<0, false, false><<<G, NTHR8, 0, stream>>>(
           a4, offsets, S, w4, N, Kd, c16, nullptr, 1, 0, 1.0f, nullptr, 1.0f);
     else
       grouped_gemm_bf16_kernel<0><<<G, NTHR, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
   } else {
     if (dma)
-      grouped_gemm_bf16_dma_kernel<1, false, false><<<G, NTHR8, 0, stream>>>(
+      grouped_gemm_dma_kernel<1, false, false><<<G, NTHR8, 0, stream>>>(
           a4, offsets, S, w4, N, Kd, c16, nullptr, 1, 0, 1.0f, nullptr, 1.0f);
     else
       grouped_gemm_bf16_kernel<1><<<G, NTHR, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
@@ -958,7 +960,7 @@ moe_status_t launch_gemm_bf16_gate_up_gathered(const void* x, int T, int K,
   if (!gemm_bf16_gather_ok(T, H)) return MOE_ERR_UNSUPPORTED;
   if (max_rows == 0) return MOE_OK;
   const int G = gemm_grid(max_rows, S, I, BROWS / 2);
-  grouped_gemm_bf16_dma_kernel<0, true, false><<<G, NTHR8, 0, stream>>>(
+  grouped_gemm_dma_kernel<0, true, false><<<G, NTHR8, 0, stream>>>(
       static_cast<const uint4*>(x), offsets, S, static_cast<const uint4*>(w), I, H, c,
       sorted_pairs, K, T, 1.0f, nullptr, 1.0f);
   return launch_status();
@@ -984,10 +986,10 @@ moe_status_t launch_gemm_fp8(moe_gemm_op_t op, const uint8_t* a, float a_scale,
   const uint4* a4 = reinterpret_cast<const uint4*>(a);
   const uint4* w4 = reinterpret_cast<const uint4*>(w);
   if (gu)
-    grouped_gemm_bf16_dma_kernel<0, false, true><<<G, NTHR8, 0, stream>>>(
+    grouped_gemm_dma_kernel<0, false, true><<<G, NTHR8, 0, stream>>>(
         a4, offsets, S, w4, N, Kd, c, nullptr, 1, 0, a_scale, w_scale, 1.0f / out_scale);
   else
-    grouped_gemm_bf16_dma_kernel<1, false, true><<<G, NTHR8, 0, stream>>>(
+    grouped_gemm_dma_kernel<1, false, true><<<G, NTHR8, 0, stream>>>(
         a4, offsets, S, w4, N, Kd, c, nullptr, 1, 0, a_scale, w_scale, 1.0f);
   return launch_status();
 }
@@ -1001,7 +1003,7 @@ moe_status_t launch_gemm_fp8_gate_up_gathered(const uint8_t* xq, int T, int K,
   if (!gemm_fp8_gather_ok(T, H)) return MOE_ERR_UNSUPPORTED;
   if (max_rows == 0) return MOE_OK;
   const int G = gemm_grid(max_rows, S, I, BROWS / 2);
-  grouped_gemm_bf16_dma_kernel<0, true, true><<<G, NTHR8, 0, stream>>>(
+  grouped_gemm_dma_kernel<0, true, true><<<G, NTHR8, 0, stream>>>(
       reinterpret_cast<const uint4*>(xq), offsets, S, reinterpret_cast<const uint4*>(w), I, H,
       c, sorted_pairs, K, T, a_scale, w_scale, 1.0f / out_scale);
   return launch_status();

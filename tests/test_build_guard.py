@@ -8,7 +8,7 @@ import pytest
 
 from moe_expert_dispatch_amd import build as b
 
-_DMA = "_ZN3moe12_GLOBAL__N_128grouped_gemm_bf16_dma_kernelILi0ELb0EEEvPK"
+_DMA = "_ZN3moe12_GLOBAL__N_123grouped_gemm_dma_kernelILi0ELb0ELb0EEEvPK"
 _REG = "_ZN3moe12_GLOBAL__N_124grouped_gemm_bf16_kernelILi0EEEvPK"
 
 
@@ -23,15 +23,15 @@ def _remarks(name, scratch, vspill):
 
 
 def test_clean_dma_kernel_passes():
-    b._check_no_scratch("gemm_bf16.hip", _remarks(_DMA, 0, 0))
+    b._check_no_scratch("gemm_mfma.hip", _remarks(_DMA, 0, 0))
 
 
 @pytest.mark.parametrize("scratch,vspill", [(4, 0), (0, 3), (16, 4)])
 def test_dma_kernel_with_scratch_is_rejected(scratch, vspill):
-    with pytest.raises(RuntimeError, match="grouped_gemm_bf16_dma_kernel"):
-        b._check_no_scratch("gemm_bf16.hip", _remarks(_DMA, scratch, vspill))
+    with pytest.raises(RuntimeError, match="grouped_gemm_dma_kernel"):
+        b._check_no_scratch("gemm_mfma.hip", _remarks(_DMA, scratch, vspill))
 
 
 def test_other_kernels_may_spill():
     # compiler-managed waits: a spill costs time, not correctness
-    b._check_no_scratch("gemm_bf16.hip", _remarks(_REG, 12, 0) + "\n" + _remarks(_DMA, 0, 0))
+    b._check_no_scratch("gemm_mfma.hip", _remarks(_REG, 12, 0) + "\n" + _remarks(_DMA, 0, 0))
