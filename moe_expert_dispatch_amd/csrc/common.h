@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe.h"
 
 namespace moe {
@@ -35,21 +37,55 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return (l == 0) ? 0ull : (~0ull >> (64 - l));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+// Wave-wide reductions without LDS traffic: DPP moves inside each 16-lane
+// row (swap lane pairs, swap pairs of pairs, mirror the half rows, mirror
+// the row), then the row-pair and half-wave swaps (v_permlane16_swap,
+// v_permlane32_swap). Every step combines a lane with exactly one partner
+// and every lane ends with the full result; for the sum, each partner pair
+// adds the same two values, so all lanes hold bit-identical totals.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppQuad1032 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuad2301 = 0x4E;   // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  v = mx(v, dpp_u32<kDppQuad1032>(v));
+  v = mx(v, dpp_u32<kDppQuad2301>(v));
+  v = mx(v, dpp_u32<kDppRowHalfMirror>(v));
+  v = mx(v, dpp_u32<kDppRowMirror>(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // {own, partner}
+  v = mx(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return mx(b[0], b[1]);
 }
 
+__device__ __forceinline__ float wave_sum(float v) {
+  auto dpp = [](float x, auto ctrl) {
+    return __uint_as_float(dpp_u32<decltype(ctrl)::value>(__float_as_uint(x)));
+  };
+  v += dpp(v, std::integral_constant<int, kDppQuad1032>{});
+  v += dpp(v, std::integral_constant<int, kDppQuad2301>{});
+  v += dpp(v, std::integral_constant<int, kDppRowHalfMirror>{});
+  v += dpp(v, std::integral_constant<int, kDppRowMirror>{});
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 64-bit maximum as two 32-bit passes: the high words, then the low words of
+// the lanes holding that high word.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, off, kWave);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, kWave);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
+  const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // ---------------------------------------------------------------- misc
