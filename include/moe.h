@@ -175,8 +175,9 @@ moe_status_t moe_slot_map(const int32_t* ids, const float* w, int T, int K, int 
  *   x_perm [T*K, H] (capacity; rows [0, P_in) written):
  *     x_perm[pair_row[p]] = x[p / K] bit for bit.
  * x [T, H] of dtype dt (f32 or bf16); H * sizeof(dt) must be a multiple of
- * 16 bytes. ws: device workspace of at least moe_permute_workspace_size()
- * bytes (per-chunk slot histograms; contents on entry are ignored).
+ * 16 bytes. ws: 16-byte aligned device workspace of at least
+ * moe_permute_workspace_size() bytes (per-chunk slot histograms; contents on
+ * entry are ignored).
  * x_perm may be NULL to compute only the index arrays.
  */
 size_t moe_permute_workspace_size(int T, int K, int S);

@@ -82,6 +82,7 @@ moe_status_t check_permute(const void* x, moe_dtype_t dt, int T, int H, int K,
   if (x_perm && T > 0 && (!x || !aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
   const size_t need = permute_plan(T, K, S).ws_bytes;
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 

@@ -9,9 +9,9 @@
 // ascending pair index. Four kernels, all deterministic:
 //   1. count   one block per chunk of pairs: LDS histogram over slots,
 //              written slot-major: hist[s * nchunks + c].
-//   2. scan    one block: exclusive scan of hist in slot-major order, which
-//              yields each (slot, chunk) base row; offsets[s] = base of
-//              (s, chunk 0) and offsets[S] = P_in.
+//   2. scan    one block, one pass: exclusive scan of hist in slot-major
+//              order, which yields each (slot, chunk) base row;
+//              offsets[s] = base of (s, chunk 0) and offsets[S] = P_in.
 //   3. scatter one block per chunk: batches of 64 pairs are ranked with a
 //              ballot per slot and per-batch counts are scanned in LDS, so
 //              the order inside a chunk is the pair order.
@@ -52,74 +52,86 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
 }
 
 constexpr int kScanThreads = 1024;
-constexpr int kScanPer = 8;                           // entries per thread per tile
-constexpr int kScanTile = kScanThreads * kScanPer;    // 8192 entries (32 KB of LDS)
+constexpr int kScanVec = 16;  // 16-byte vectors per thread: 64 entries, and
+                              // S * nchunks <= 65536 (permute_plan)
 
-// Exclusive scan of hist[0..S*nchunks) in place, in tiles staged through LDS
-// (coalesced loads, all of a tile's loads in flight together).
+// Exclusive scan of hist[0..N) in place, N = S * nchunks, in one pass: thread
+// t owns the contiguous entries [t * per, (t + 1) * per) (per a multiple of 4,
+// at most 64), loads them with up to 16 vector loads all in flight, and one
+// block scan of the per-thread sums gives every thread its base. The
+// workspace is padded to whole vectors; entries at or past N count as 0 and
+// are not written.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict__ hist, int S,
                                                             int nchunks,
                                                             int32_t* __restrict__ offsets) {
-  __shared__ int32_t tile[kScanTile];
   __shared__ int32_t wsum[kScanThreads / kWave];
   const int N = S * nchunks;
+  const int per = 4 * ceil_div(N, 4 * kScanThreads);
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
-  int carry = 0;
-  for (int base = 0; base < N; base += kScanTile) {
-    const int n = min(kScanTile, N - base);
+  const int lo = tid * per;
+  int4 q[kScanVec];
 #pragma unroll
-    for (int k = 0; k < kScanPer; ++k) {
-      const int i = k * kScanThreads + tid;
-      tile[i] = i < n ? hist[base + i] : 0;
-    }
-    __syncthreads();
-    int v[kScanPer];
-    int sum = 0;
-#pragma unroll
-    for (int k = 0; k < kScanPer; ++k) {
-      v[k] = tile[tid * kScanPer + k];
-      sum += v[k];
-    }
-    // inclusive scan of the per-thread sums: within the wave, then across waves
-    int incl = sum;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int o = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += o;
-    }
-    if (lane == kWave - 1) wsum[wave] = incl;
-    __syncthreads();
-    if (wave == 0) {
-      int w = lane < kScanThreads / kWave ? wsum[lane] : 0;
-#pragma unroll
-      for (int off = 1; off < kScanThreads / kWave; off <<= 1) {
-        const int o = __shfl_up(w, off, kWave);
-        if (lane >= off) w += o;
-      }
-      if (lane < kScanThreads / kWave) wsum[lane] = w;
-    }
-    __syncthreads();
-    int run = carry + incl - sum + (wave > 0 ? wsum[wave - 1] : 0);
-#pragma unroll
-    for (int k = 0; k < kScanPer; ++k) {
-      tile[tid * kScanPer + k] = run;
-      run += v[k];
-    }
-    const int tile_total = wsum[kScanThreads / kWave - 1];
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kScanPer; ++k) {
-      const int i = k * kScanThreads + tid;
-      if (i < n) hist[base + i] = tile[i];
-    }
-    carry += tile_total;
-    __syncthreads();
+  for (int k = 0; k < kScanVec; ++k) {
+    const int i = lo + 4 * k;
+    q[k] = (4 * k < per && i < N) ? *reinterpret_cast<const int4*>(hist + i)
+                                   : make_int4(0, 0, 0, 0);
   }
+  int sum = 0;
+#pragma unroll
+  for (int k = 0; k < kScanVec; ++k) {
+    const int i = lo + 4 * k;
+    const bool in = 4 * k < per;
+    q[k].x = in && i < N ? q[k].x : 0;
+    q[k].y = in && i + 1 < N ? q[k].y : 0;
+    q[k].z = in && i + 2 < N ? q[k].z : 0;
+    q[k].w = in && i + 3 < N ? q[k].w : 0;
+    sum += q[k].x + q[k].y + q[k].z + q[k].w;
+  }
+  // inclusive scan of the per-thread sums: within the wave, then across waves
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kScanThreads / kWave ? wsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kScanThreads / kWave; off <<= 1) {
+      const int o = __shfl_up(w, off, kWave);
+      if (lane >= off) w += o;
+    }
+    if (lane < kScanThreads / kWave) wsum[lane] = w;
+  }
+  __syncthreads();
+  int run = incl - sum + (wave > 0 ? wsum[wave - 1] : 0);
+#pragma unroll
+  for (int k = 0; k < kScanVec; ++k) {
+    const int i = lo + 4 * k;
+    if (4 * k < per && i < N) {
+      int4 e;
+      e.x = run;
+      e.y = e.x + q[k].x;
+      e.z = e.y + q[k].y;
+      e.w = e.z + q[k].z;
+      run = e.w + q[k].w;
+      if (i + 3 < N) {
+        *reinterpret_cast<int4*>(hist + i) = e;
+      } else {
+        hist[i] = e.x;
+        if (i + 1 < N) hist[i + 1] = e.y;
+        if (i + 2 < N) hist[i + 2] = e.z;
+      }
+    }
+  }
+  __syncthreads();  // the scanned entries are visible to the whole block
   for (int s = tid; s < S; s += kScanThreads)
     offsets[s] = nchunks > 0 ? hist[(size_t)s * nchunks] : 0;
-  if (tid == 0) offsets[S] = carry;
+  if (tid == 0) offsets[S] = wsum[kScanThreads / kWave - 1];
 }
 
 // One block (4 waves) per chunk. The chunk is walked in sub-chunks of 512
@@ -271,7 +283,8 @@ PermutePlan permute_plan(int T, int K, int S) {
   pl.chunk = kSub * (n > 0 ? ceil_div(units, n) : 1);
   pl.nchunks = pl.P > 0 ? ceil_div(pl.P, pl.chunk) : 0;
   const int bound = n > 0 ? n : 1;  // min(units, cap), monotone in P
-  pl.ws_bytes = (size_t)S * (size_t)bound * sizeof(int32_t);
+  // histograms, padded to whole 16-byte vectors for the scan
+  pl.ws_bytes = ((size_t)S * (size_t)bound * sizeof(int32_t) + 15) / 16 * 16;
   return pl;
 }
 
@@ -280,6 +293,9 @@ moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
                             int32_t* sorted_pairs, int32_t* pair_row, void* x_perm, void* ws,
                             hipStream_t stream, int seg_cap, const float* pair_w) {
   const PermutePlan pl = permute_plan(T, K, S);
+  // the one-pass scan covers up to 64 entries per thread
+  if ((long long)S * pl.nchunks > (long long)kScanThreads * 4 * kScanVec)
+    return MOE_ERR_UNSUPPORTED;
   int32_t* hist = static_cast<int32_t*>(ws);
   const size_t lds = (size_t)S * sizeof(int32_t);
   if (pl.nchunks > 0) {
