@@ -337,11 +337,11 @@ def main():
                    "intermediate": cfg.I, "experts": cfg.E, "slots": S, "top_k": cfg.K,
                    "renormalize": cfg.renormalize, "ep_size": cfg.ep_size, "ep_rank": rank,
                    "included_pairs": P_in, "parallelism": "single GPU"},
-        "roofline": ({"bound": "mfma", "kernel": "grouped_gemm_bf16 gate/up + SwiGLU",
+        "roofline": ({"bound": "mfma", "kernel": "grouped_gemm_dma_kernel bf16 gate/up + SwiGLU",
                       "achieved": gu_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                       "frac": gu_tflops / PEAK_BF16_TFLOPS, "traffic": traffic}
                      if cfg.dtype == "bf16" else
-                     {"bound": "mfma", "kernel": "grouped_gemm fp8 (E4M3) gate/up + SwiGLU",
+                     {"bound": "mfma", "kernel": "grouped_gemm_dma_kernel FP8 (E4M3) gate/up + SwiGLU",
                       "achieved": gu_tflops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                       "frac": gu_tflops / PEAK_FP8_TFLOPS, "traffic": traffic}
                      if fp8 else
