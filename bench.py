@@ -138,6 +138,17 @@ def run_a2a(args):
     print(json.dumps(res), flush=True)
 
 
+def kernel_source_digest(path):
+    """SHA-256 of a source file with its comments and whitespace removed: it
+    changes when the code does, not when a comment does."""
+    import re
+    with open(path) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return hashlib.sha256(re.sub(r"\s+", "", src).encode()).hexdigest()
+
+
 def gemm_traffic(workload):
     """HBM traffic of grouped GEMM 1 from the committed profiler summary, or
     None if the kernel source changed since the counters were taken or they
@@ -145,8 +156,7 @@ def gemm_traffic(workload):
     try:
         with open(os.path.join(TRAFFIC_DIR, f"{workload}_gate_up_traffic.json")) as f:
             rec = json.load(f)
-        with open(GEMM_SRC, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = kernel_source_digest(GEMM_SRC)
         if rec.get("kernel_source_sha256") != sha or rec.get("workload") != workload:
             return None
         return rec.get("bytes_per_launch")

@@ -360,11 +360,13 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS kernel, used when K % 64 == 0 and K >= 128. Same tiles, item
-// order and SwiGLU as above, with 8 waves (two per SIMD, so each SIMD has two
+// Direct-to-LDS kernel, used for bf16 when K % 64 == 0 and K >= 128, and for
+// every FP8 product (K % 128 == 0, K >= 256). Same tiles, item order and
+// SwiGLU as above, with 8 waves (two per SIMD, so each SIMD has two
 // instruction streams) in a 2 x 4 layout of 128 x 64 wave tiles, and the
 // operands moved by buffer_load_dwordx4 ... lds: no registers hold
-// prefetched data.
+// prefetched data. The schedule below is the bf16 one; the FP8 slice
+// schedule is described with its fragments further down.
 //
 // LDS holds two buffers of one 64-wide K-slice each (64 KB: 256 activation
 // rows and 256 weight rows of 128 bytes). Chunk c of row r sits at
