@@ -263,3 +263,51 @@ def test_forward_full_size_sampled(dev):
     got = np64(out[torch.from_numpy(tokens).to(dev)].cpu())
     ref = _oracle(inp, tokens=tokens)
     assert_close(got, ref, BF16_TOL, "redundant_slots_zipf_fp8")
+
+
+def test_forward_ep_accumulate_f32(dev):
+    """The EP shares accumulated on the device into one f32 output equal the
+    full FP8 layer (the partial-sum identity with FP8 experts)."""
+    cfg = WorkloadConfig("fp8_ep_acc", T=257, H=256, I=256, E=16, K=3, renormalize=True,
+                         dtype="fp8", router="gauss_bias", bias_std=0.5, ep_size=4, seed=43)
+    inp = make_inputs(cfg)
+    announce("fp8 forward: 4 EP shares accumulated in f32")
+    out = torch.zeros(cfg.T, cfg.H, dtype=torch.float32, device=dev)
+    for r in range(cfg.ep_size):
+        wgu, wd, sgu, sd, ro, rs, S = _share(inp, dev, ep_rank=r)
+        fc = moe.ForwardConfig(T=cfg.T, H=cfg.H, I=cfg.I, E_global=cfg.E, K=cfg.K,
+                               renormalize=True, S=S, dtype=moe.FP8, out_dtype=torch.float32,
+                               ep_size=cfg.ep_size, ep_rank=r, accumulate=True,
+                               a1_scale=cfg.a1_scale, a2_scale=cfg.a2_scale)
+        moe.forward(fc, inp.x.to(dev), wgu, wd, logits=inp.logits.to(dev), rep_off=ro,
+                    rep_slots=rs, out=out, w_gate_up_scale=sgu, w_down_scale=sd)
+    torch.cuda.synchronize()
+    full = oracle.fp8_forward(inp.x, inp.logits, inp.w_gate_up.numpy(), inp.w_gate_up_scale,
+                              inp.w_down.numpy(), inp.w_down_scale, cfg.a1_scale, cfg.a2_scale,
+                              cfg.K, True)
+    assert_close(np64(out.cpu()), full, BF16_TOL, "fp8 EP accumulate")
+
+
+def test_forward_grouped_routing_topk_form(dev):
+    """Group-limited routing from logits, and the oracle's routing passed as
+    precomputed experts and weights, both match the FP8 oracle."""
+    cfg = small("deepseek_v2_fp8", 300, H=256, I=384)
+    cfg = cfg.replace(num_expert_group=8, topk_group=3)
+    inp = make_inputs(cfg)
+    announce("fp8 forward: grouped routing, logits and top-k forms")
+    wgu, wd, sgu, sd, ro, rs, S = _share(inp, dev)
+    fc = moe.ForwardConfig(T=cfg.T, H=cfg.H, I=cfg.I, E_global=cfg.E, K=cfg.K,
+                           renormalize=True, S=S, dtype=moe.FP8, num_expert_group=8,
+                           topk_group=3, a1_scale=cfg.a1_scale, a2_scale=cfg.a2_scale)
+    kw = dict(rep_off=ro, rep_slots=rs, w_gate_up_scale=sgu, w_down_scale=sd)
+    out = moe.forward(fc, inp.x.to(dev), wgu, wd, logits=inp.logits.to(dev), **kw)
+    ids, w = oracle.route_grouped(inp.logits.numpy(), cfg.K, True, 8, 3)
+    out2 = moe.forward(fc, inp.x.to(dev), wgu, wd,
+                       topk_ids=torch.from_numpy(ids.astype(np.int32)).to(dev),
+                       topk_w=torch.from_numpy(w.astype(np.float32)).to(dev), **kw)
+    torch.cuda.synchronize()
+    ref = oracle.fp8_forward(inp.x, None, inp.w_gate_up.numpy(), inp.w_gate_up_scale,
+                             inp.w_down.numpy(), inp.w_down_scale, cfg.a1_scale, cfg.a2_scale,
+                             cfg.K, False, topk=(ids, w))
+    assert_close(np64(out.cpu()), ref, BF16_TOL, "fp8 grouped routing")
+    assert_close(np64(out2.cpu()), ref, BF16_TOL, "fp8 grouped routing, top-k form")
