@@ -414,6 +414,11 @@ __device__ __forceinline__ void lds_read16(int32x4_t& d, uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF));
 }
 
+template <int OFF>
+__device__ __forceinline__ void lds_write16(uint32_t addr, int32x4_t v) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "n"(OFF));
+}
+
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
@@ -600,14 +605,16 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
   // exchanged between the lane halves, after which lane l holds 8
   // consecutive columns of row l mod 32 (group g for l < 32, g+1 above) and
   // writes them as one 16-byte store.
-  auto store8 = [&](const WItem& x, uint32_t r, int col, const float* lo, const float* hi) {
+  auto pack8 = [&](const float* lo, const float* hi) {
     uint32_t x0 = pack_bf16x2(lo[0], lo[1]), x1 = pack_bf16x2(lo[2], lo[3]);
     uint32_t y0 = pack_bf16x2(hi[0], hi[1]), y1 = pack_bf16x2(hi[2], hi[3]);
     const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
     const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+    return int32x4_t{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+  };
+  auto store8 = [&](const WItem& x, uint32_t r, int col, const float* lo, const float* hi) {
     __builtin_amdgcn_raw_buffer_store_b128(
-        int32x4_t{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]}, x.rc,
-        col < N ? (r * (uint32_t)N + (uint32_t)col) * 2u : kOOB, 0, 0);
+        pack8(lo, hi), x.rc, col < N ? (r * (uint32_t)N + (uint32_t)col) * 2u : kOOB, 0, 0);
   };
   // FP8 output: 4 + 4 codes per lane exchanged like store8, one 8-byte store.
   auto store8q = [&](const WItem& x, uint32_t r, int col, const float* lo, const float* hi) {
@@ -620,7 +627,86 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
         int32x2_t{(int)q[0], (int)q[1]}, x.rc,
         col < N ? r * (uint32_t)N + (uint32_t)col : kOOB, 0, 0);
   };
+  // bf16 down product: a lane's 16-byte pieces cover 32 bytes of a row per
+  // store, so each wave first writes its 128 x 64 tile (bf16, rows of 128 bytes,
+  // chunk c of row r at c ^ ((r >> 1) & 7)) into its own 16 KB of the idle
+  // stages, then reads it back as 8 rows x 8 chunks per instruction and
+  // stores whole 128-byte lines. Reads and writes are conflict-free (each
+  // half-wave touches every 16-byte bank group twice). The caller keeps the
+  // next item's DMA behind a barrier until every wave has read its tile.
+  // (The FP8 down kernel stores directly: the staging addresses do not fit
+  // beside its K-loop's registers without spilling.)
+  constexpr bool STAGED = OP == 1 && !FP8;
+  auto epilogue_down = [&](const WItem& x) {
+    // addresses derived per item from the lane index recomputed here (opaque
+    // to the compiler), so that neither it nor anything derived from it is
+    // held in a register across the K-loop
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const uint32_t eb = smem_base + (uint32_t)wave * 16384u;
+    const uint32_t p = (uint32_t)((ln >> 5) ^ ((ln >> 1) & 7));
+    const uint32_t wrow = eb + (uint32_t)(ln & 31) * 128u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // (g, j) = (0, 0), (2, 0), (0, 1), (2, 1)
+      const int g = 2 * (q & 1), j = q >> 1;
+      const uint32_t wa = wrow + (((uint32_t)(g + 4 * j) ^ p) * 16u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float o[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          o[v] = acc[j][i][4 * g + v];
+          if constexpr (FP8) o[v] *= x.sc;
+        }
+        const int32x4_t val = pack8(o, o + 4);
+        switch (i) {  // rows 32 i .. 32 i + 31: an immediate offset
+          case 0: lds_write16<0 * 4096>(wa, val); break;
+          case 1: lds_write16<1 * 4096>(wa, val); break;
+          case 2: lds_write16<2 * 4096>(wa, val); break;
+          default: lds_write16<3 * 4096>(wa, val); break;
+        }
+      }
+    }
+    // instruction t reads rows 8t .. 8t+7: row 8t + lane/8, chunk lane % 8
+    // (addresses again from an opaque lane index, computed after the writes)
+    asm volatile("" : "+v"(ln));
+    const uint32_t c = (uint32_t)(ln & 7);
+    const uint32_t rbase = eb + (uint32_t)(ln >> 3) * 128u;
+    const uint32_t ra0 = rbase + ((c ^ (uint32_t)(ln >> 4)) * 16u);
+    const uint32_t ra1 = rbase + ((c ^ (uint32_t)(4 | (ln >> 4))) * 16u);
+    const int col = x.col0 + wn * 64 + 8 * (int)c;
+    const bool col_ok = col < N;
+    uint32_t nb = (uint32_t)N * 2u;  // row pitch in bytes, opaque like ln
+    asm volatile("" : "+s"(nb));
+    // byte offset of row wm*128 + lane/8, column col; +8 rows per instruction
+    const uint32_t obase = (uint32_t)(wm * 128 + (ln >> 3)) * nb + (uint32_t)col * 2u;
+    auto half = [&](auto hc) {  // rows 64h .. 64h + 63
+      constexpr int h = decltype(hc)::value;
+      int32x4_t v[8];
+      lds_read16<(8 * h + 0) * 1024>(v[0], ra0);
+      lds_read16<(8 * h + 1) * 1024>(v[1], ra1);
+      lds_read16<(8 * h + 2) * 1024>(v[2], ra0);
+      lds_read16<(8 * h + 3) * 1024>(v[3], ra1);
+      lds_read16<(8 * h + 4) * 1024>(v[4], ra0);
+      lds_read16<(8 * h + 5) * 1024>(v[5], ra1);
+      lds_read16<(8 * h + 6) * 1024>(v[6], ra0);
+      lds_read16<(8 * h + 7) * 1024>(v[7], ra1);
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                     "+v"(v[6]), "+v"(v[7]));
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            v[u], x.rc, col_ok ? obase + (uint32_t)(8 * (8 * h + u)) * nb : kOOB, 0, 0);
+    };
+    half(std::integral_constant<int, 0>{});
+    half(std::integral_constant<int, 1>{});
+  };
   auto epilogue = [&](const WItem& x) {
+    if constexpr (STAGED) {
+      epilogue_down(x);
+      return;
+    }
     const int ch = 8 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -883,6 +969,8 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
         vm_wait<0>();
       }
       epilogue(done);
+      // down: every wave has read its staged tile before the next DMA
+      if constexpr (STAGED) __builtin_amdgcn_s_barrier();
     } else {
       for (int d = 0; d < dlast; ++d) pass_step(d);
       if constexpr (GATHER) {
@@ -892,6 +980,7 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
       vm_wait<0>();
       __builtin_amdgcn_s_barrier();
       if constexpr (!GATHER) next_setup();
+      if constexpr (STAGED) __builtin_amdgcn_s_barrier();  // the computing waves' second one
     }
     if (has_next) {
       gather_offsets(cur);
