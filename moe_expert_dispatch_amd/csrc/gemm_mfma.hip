@@ -389,8 +389,11 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_kernel(
 //               buffer d & 1) and one LDS read of block 0 of slice d+1.
 // Every slice issues the same 8 DMA instructions per wave (slices past the
 // end use an out-of-range offset and move nothing), so the vmcnt accounting
-// is constant. An item's epilogue stores are issued before the next item's
-// first two slices, so the wait for slice 0 also covers them.
+// is constant. The next item's first two slices (only slice 0 for the staged
+// bf16 down epilogue, which occupies stage 1) are requested before an item's
+// epilogue stores, so their fetch overlaps the epilogue. The wait for slice 0
+// is then vmcnt(8): the 8 DMAs of slice 1 are younger, and loads complete in
+// order, so whatever the stores do, no DMA of slice 0 can be outstanding.
 constexpr int NTHR8 = 512;  // 8 waves: 2 per SIMD
 constexpr int WBK = 64;
 constexpr int WA_VEC = BM * WBK / 8;                // 2048 vectors: A part of a stage
@@ -568,11 +571,13 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
           (live && x.b_off[i] != kOOB) ? x.b_off[i] + kb : kOOB, 0, 0, 0);
     }
   };
+  auto issue_slice = [&](const WItem& x, int d) {
+#pragma unroll
+    for (int q = 0; q < WDMA; ++q) dma(x, q, d);
+  };
   auto issue_prologue = [&](const WItem& x) {
-#pragma unroll
-    for (int d = 0; d < 2; ++d)
-#pragma unroll
-      for (int q = 0; q < WDMA; ++q) dma(x, q, d);
+    issue_slice(x, 0);
+    issue_slice(x, 1);
   };
 
   floatx16 acc[2][4];
@@ -628,48 +633,46 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
         col < N ? r * (uint32_t)N + (uint32_t)col : kOOB, 0, 0);
   };
   // bf16 down product: a lane's 16-byte pieces cover 32 bytes of a row per
-  // store, so each wave first writes its 128 x 64 tile (bf16, rows of 128 bytes,
-  // chunk c of row r at c ^ ((r >> 1) & 7)) into its own 16 KB of the idle
-  // stages, then reads it back as 8 rows x 8 chunks per instruction and
+  // store, so each wave writes its 128 x 64 tile, 64 rows at a time (bf16,
+  // rows of 128 bytes, chunk c of row r at c ^ ((r >> 1) & 7)), into its own
+  // 8 KB of stage 1, reads it back as 8 rows x 8 chunks per instruction and
   // stores whole 128-byte lines. Reads and writes are conflict-free (each
-  // half-wave touches every 16-byte bank group twice). The caller keeps the
-  // next item's DMA behind a barrier until every wave has read its tile.
+  // half-wave touches every 16-byte bank group twice). Stage 0 is left to
+  // the next item's first K-slice, whose DMA is issued before this epilogue;
+  // the caller keeps the DMA of the second slice (into stage 1) behind a
+  // barrier until every wave has read its tile.
   // (The FP8 down kernel stores directly: the staging addresses do not fit
   // beside its K-loop's registers without spilling.)
   constexpr bool STAGED = OP == 1 && !FP8;
+  // The next item's slice 0 is requested before this item's epilogue stores,
+  // except in the gathered bf16 gate/up kernel, whose SwiGLU epilogue has no
+  // registers left for it.
+  constexpr bool EARLY = !(GATHER && !FP8);
+  auto issue_next = [&](const WItem& x, auto before_epilogue) {
+    if constexpr (decltype(before_epilogue)::value) {
+      if constexpr (EARLY) {
+        gather_offsets(cur);
+        issue_slice(x, 0);
+      }
+    } else {
+      if constexpr (!EARLY) {
+        gather_offsets(cur);
+        issue_slice(x, 0);
+      }
+      issue_slice(x, 1);
+    }
+  };
   auto epilogue_down = [&](const WItem& x) {
     // addresses derived per item from the lane index recomputed here (opaque
     // to the compiler), so that neither it nor anything derived from it is
     // held in a register across the K-loop
     int ln;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-    const uint32_t eb = smem_base + (uint32_t)wave * 16384u;
+    const uint32_t eb = smem_base + (uint32_t)WSTAGE_BYTES + (uint32_t)wave * 8192u;
     const uint32_t p = (uint32_t)((ln >> 5) ^ ((ln >> 1) & 7));
     const uint32_t wrow = eb + (uint32_t)(ln & 31) * 128u;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {  // (g, j) = (0, 0), (2, 0), (0, 1), (2, 1)
-      const int g = 2 * (q & 1), j = q >> 1;
-      const uint32_t wa = wrow + (((uint32_t)(g + 4 * j) ^ p) * 16u);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float o[8];
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          o[v] = acc[j][i][4 * g + v];
-          if constexpr (FP8) o[v] *= x.sc;
-        }
-        const int32x4_t val = pack8(o, o + 4);
-        switch (i) {  // rows 32 i .. 32 i + 31: an immediate offset
-          case 0: lds_write16<0 * 4096>(wa, val); break;
-          case 1: lds_write16<1 * 4096>(wa, val); break;
-          case 2: lds_write16<2 * 4096>(wa, val); break;
-          default: lds_write16<3 * 4096>(wa, val); break;
-        }
-      }
-    }
-    // instruction t reads rows 8t .. 8t+7: row 8t + lane/8, chunk lane % 8
-    // (addresses again from an opaque lane index, computed after the writes)
-    asm volatile("" : "+v"(ln));
+    // instruction t of a half reads its rows 8t .. 8t+7: row 8t + lane/8,
+    // chunk lane % 8
     const uint32_t c = (uint32_t)(ln & 7);
     const uint32_t rbase = eb + (uint32_t)(ln >> 3) * 128u;
     const uint32_t ra0 = rbase + ((c ^ (uint32_t)(ln >> 4)) * 16u);
@@ -680,17 +683,36 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
     asm volatile("" : "+s"(nb));
     // byte offset of row wm*128 + lane/8, column col; +8 rows per instruction
     const uint32_t obase = (uint32_t)(wm * 128 + (ln >> 3)) * nb + (uint32_t)col * 2u;
-    auto half = [&](auto hc) {  // rows 64h .. 64h + 63
+    auto half = [&](auto hc) {  // accumulator rows 64h .. 64h + 63
       constexpr int h = decltype(hc)::value;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {  // (g, j) = (0, 0), (2, 0), (0, 1), (2, 1)
+        const int g = 2 * (q & 1), j = q >> 1;
+        const uint32_t wa = wrow + (((uint32_t)(g + 4 * j) ^ p) * 16u);
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = 2 * h + ii;
+          float o[8];
+#pragma unroll
+          for (int v = 0; v < 8; ++v) o[v] = acc[j][i][4 * g + v];
+          const int32x4_t val = pack8(o, o + 4);
+          if (ii == 0)
+            lds_write16<0>(wa, val);
+          else
+            lds_write16<4096>(wa, val);
+        }
+      }
+      // the previous half's reads completed before its stores (wait below),
+      // and LDS operations of one wave run in order
       int32x4_t v[8];
-      lds_read16<(8 * h + 0) * 1024>(v[0], ra0);
-      lds_read16<(8 * h + 1) * 1024>(v[1], ra1);
-      lds_read16<(8 * h + 2) * 1024>(v[2], ra0);
-      lds_read16<(8 * h + 3) * 1024>(v[3], ra1);
-      lds_read16<(8 * h + 4) * 1024>(v[4], ra0);
-      lds_read16<(8 * h + 5) * 1024>(v[5], ra1);
-      lds_read16<(8 * h + 6) * 1024>(v[6], ra0);
-      lds_read16<(8 * h + 7) * 1024>(v[7], ra1);
+      lds_read16<0 * 1024>(v[0], ra0);
+      lds_read16<1 * 1024>(v[1], ra1);
+      lds_read16<2 * 1024>(v[2], ra0);
+      lds_read16<3 * 1024>(v[3], ra1);
+      lds_read16<4 * 1024>(v[4], ra0);
+      lds_read16<5 * 1024>(v[5], ra1);
+      lds_read16<6 * 1024>(v[6], ra0);
+      lds_read16<7 * 1024>(v[7], ra1);
       asm volatile("s_waitcnt lgkmcnt(0)"
                    : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
                      "+v"(v[6]), "+v"(v[7]));
@@ -968,8 +990,9 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
         next_setup();
         vm_wait<0>();
       }
+      if (has_next) issue_next(cur, std::true_type{});
       epilogue(done);
-      // down: every wave has read its staged tile before the next DMA
+      // staged down: every wave has read its tile before slice 1 enters stage 1
       if constexpr (STAGED) __builtin_amdgcn_s_barrier();
     } else {
       for (int d = 0; d < dlast; ++d) pass_step(d);
@@ -980,12 +1003,10 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
       vm_wait<0>();
       __builtin_amdgcn_s_barrier();
       if constexpr (!GATHER) next_setup();
+      if (has_next) issue_next(cur, std::true_type{});
       if constexpr (STAGED) __builtin_amdgcn_s_barrier();  // the computing waves' second one
     }
-    if (has_next) {
-      gather_offsets(cur);
-      issue_prologue(cur);
-    }
+    if (has_next) issue_next(cur, std::false_type{});
     item = nxt;
   }
   vm_wait<0>();
