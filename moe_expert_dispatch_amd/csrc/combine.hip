@@ -20,10 +20,18 @@ namespace {
 
 typedef int int32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kVec = 2;  // 8-element vectors per thread
+constexpr int kNonTemporal = 2;
 
 // Buffer resource over one row of Y: [row, row + bytes). A resource of 0
 // bytes (an excluded pair) makes every load return zeros without a memory
 // access, so the loads need no branch.
+//
+// Y is read exactly once, so its loads carry the non-temporal cache policy
+// (bit 1 of the buffer instruction's cache-policy operand, NT on gfx950):
+// streamed rows do not displace other lines from L2. Measured on 1.07 GB of
+// rows gathered in random order: 5.0 TB/s with the default policy, 5.8 TB/s
+// non-temporal, against 6.4 TB/s for a plain sequential read of the same
+// bytes.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0, (int)bytes,
                                            0x00020000);
@@ -31,7 +39,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, uint
 
 __device__ __forceinline__ void load8(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint16_t*,
                                       float* v) {
-  const int32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  const int32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNonTemporal);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     v[2 * i] = bf16_to_f32((uint32_t)q[i] & 0xffffu);
@@ -41,8 +49,9 @@ __device__ __forceinline__ void load8(__amdgpu_buffer_rsrc_t r, uint32_t off, co
 
 __device__ __forceinline__ void load8(__amdgpu_buffer_rsrc_t r, uint32_t off, const float*,
                                       float* v) {
-  const int32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-  const int32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16u), 0, 0);
+  const int32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNonTemporal);
+  const int32x4_t b =
+      __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16u), 0, kNonTemporal);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     v[i] = __int_as_float(a[i]);
