@@ -460,7 +460,11 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int wave = tid / kWave;  // 0..7
+  // 0..7. bf16 gate/up: in a scalar register, so the DMAs' LDS destinations
+  // (M0) are scalar arithmetic (0.7% faster on the redundant-slot layer). The
+  // down kernel measured 0.6% slower that way, and the FP8 kernels have no
+  // scalar registers to spare (they spill).
+  const int wave = (FP8 || OP == 1) ? tid / kWave : uniform(tid / kWave);
   const int wm = uniform(wave >> 2);  // 128-row half of the tile
   const int wn = wave & 3;       // quarter of the weight rows
   const size_t w_rows = (OP == 0) ? 2 * (size_t)N : (size_t)N;
