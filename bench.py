@@ -164,6 +164,26 @@ def gemm_traffic(workload):
         return None
 
 
+def staged_permute_ms(moe, x, slot, mask, S, reps=10):
+    """Device time of one moe_permute call with its row gather (x_perm
+    written), averaged over `reps` calls on the current stream."""
+    import torch
+    T, K = slot.shape
+    ws = torch.empty(max(moe.permute_workspace_size(T, K, S), 1), dtype=torch.uint8,
+                     device=x.device)
+    for _ in range(2):
+        moe.permute(x, slot, mask, S, ws=ws)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        moe.permute(x, slot, mask, S, ws=ws)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def cpu_baseline(inp, seconds, rank=0):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -330,6 +350,13 @@ def main():
     gemm_ms = stage_ms["gemm_gate_up"] + stage_ms["gemm_down"]
     traffic = gemm_traffic(cfg.name) if cfg.dtype in ("bf16", "fp8") else None
 
+    # The standalone permutation with its row gather, timed after (not inside)
+    # the steps: moe_forward folds the gather into the gate/up GEMM, so this is
+    # where the permutation's HBM rate is measured.
+    sp_ms = staged_permute_ms(moe, x, slot, mask, S)
+    xb = x.element_size()
+    sp_bytes = 2 * 5 * P + 4 * P + 4 * P_in + cfg.T * cfg.H * xb + P_in * cfg.H * xb
+
     res = {
         "metric": METRIC,
         "value": cfg.T / (ms_per_step * 1e-3),
@@ -365,6 +392,14 @@ def main():
         "grouped_gemm_frac_of_roofline": gemm_floor_ms / gemm_ms,
         "stage_ms": stage_ms,
         "permute_gbps": permute_bytes / (stage_ms["permute"] * 1e6),
+        "permute_stage_moves": ("indices only (row gather folded into the gate/up GEMM)"
+                                if fused_gather and not fp8 else
+                                "indices and quantized x" if fp8 else "indices and rows"),
+        "staged_permute": {"call": "moe_permute with its row gather, outside the timed steps",
+                           "ms": sp_ms, "bytes": sp_bytes,
+                           "gbps": sp_bytes / (sp_ms * 1e6),
+                           "frac_of_hbm": sp_bytes / (sp_ms * 1e6) / PEAK_HBM_GBPS},
+        "combine_frac_of_hbm": combine_bytes / (stage_ms["combine"] * 1e6) / PEAK_HBM_GBPS,
         "combine_gbps": combine_bytes / (stage_ms["combine"] * 1e6),
         "host_wall_ms_per_step": wall * 1e3 / args.steps,
         "input_generation_s": gen_s,

@@ -211,6 +211,31 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   }
 }
 
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): an offset at or past the end
+// reads zeros and drops stores, so vector tails need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// The permuted rows are written once and read by a later kernel, long after
+// they would have left the caches, so their stores carry the non-temporal
+// policy (bit 1 of the cache-policy operand, NT on gfx950). Measured on
+// 16384 tokens x 8 rows of 8 KB scattered in random order: 235 us with the
+// default policy, 209 us non-temporal (non-temporal loads of x as well: 252).
+constexpr int kNonTemporal = 2;
+constexpr int kGatherVec = 2;  // 16-byte vectors per thread loaded before the stores
+
+// One block per token: the token's row is loaded once (kGatherVec vectors
+// per thread, all in flight), then stored to each included pair's row.
+// scale_row (below) gives input-side routing its weighted rows.
+template <bool SCALED, typename ET>
+__device__ __forceinline__ void gather_rows(const uint4* __restrict__ x, int nvec, int K,
+                                            const int32_t* rows, const float* ws,
+                                            uint4* __restrict__ x_perm);
+
 __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x, int T,
                                                      int nvec, int K,
                                                      const int32_t* __restrict__ pair_row,
@@ -219,31 +244,56 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x
   __shared__ int32_t rows[MOE_MAX_TOPK];
   if (threadIdx.x < K) rows[threadIdx.x] = pair_row[(size_t)t * K + threadIdx.x];
   __syncthreads();
-  const uint4* src = x + (size_t)t * nvec;
-  for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
-    const uint4 val = src[v];
-    for (int k = 0; k < K; ++k) {
-      const int r = rows[k];
-      if (r >= 0) x_perm[(size_t)r * nvec + v] = val;
-    }
-  }
+  gather_rows<false, uint16_t>(x + (size_t)t * nvec, nvec, K, rows, nullptr, x_perm);
 }
 
 // Input-side routing: the row of pair (t, k) is x[t] scaled by the pair's
 // weight, w * x evaluated in f32 and rounded once to the element type.
-__device__ __forceinline__ uint4 scale_row(uint4 v, float s, const uint16_t*) {
-  uint32_t q[4] = {v.x, v.y, v.z, v.w};
+__device__ __forceinline__ int32x4_t scale_row(int32x4_t v, float s, const uint16_t*) {
+  int32x4_t o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    q[i] = pack_bf16x2(bf16_to_f32(q[i] & 0xffffu) * s, bf16_to_f32(q[i] >> 16) * s);
-  return make_uint4(q[0], q[1], q[2], q[3]);
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t q = (uint32_t)v[i];
+    o[i] = (int)pack_bf16x2(bf16_to_f32(q & 0xffffu) * s, bf16_to_f32(q >> 16) * s);
+  }
+  return o;
 }
 
-__device__ __forceinline__ uint4 scale_row(uint4 v, float s, const float*) {
-  return make_uint4(__float_as_uint(__uint_as_float(v.x) * s),
-                    __float_as_uint(__uint_as_float(v.y) * s),
-                    __float_as_uint(__uint_as_float(v.z) * s),
-                    __float_as_uint(__uint_as_float(v.w) * s));
+__device__ __forceinline__ int32x4_t scale_row(int32x4_t v, float s, const float*) {
+  int32x4_t o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = __float_as_int(__int_as_float(v[i]) * s);
+  return o;
+}
+
+template <bool SCALED, typename ET>
+__device__ __forceinline__ void gather_rows(const uint4* __restrict__ src, int nvec, int K,
+                                            const int32_t* rows, const float* ws,
+                                            uint4* __restrict__ x_perm) {
+  const uint32_t row_bytes = (uint32_t)nvec * 16u;
+  const __amdgpu_buffer_rsrc_t sr = row_rsrc(src, row_bytes);
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += kGatherVec * blockDim.x) {
+    int32x4_t val[kGatherVec];
+#pragma unroll
+    for (int u = 0; u < kGatherVec; ++u) {
+      const int v = v0 + u * blockDim.x;
+      val[u] = __builtin_amdgcn_raw_buffer_load_b128(sr, v < nvec ? (uint32_t)v * 16u : row_bytes,
+                                                     0, 0);
+    }
+    for (int k = 0; k < K; ++k) {
+      const int r = rows[k];
+      if (r < 0) continue;  // block-uniform
+      const __amdgpu_buffer_rsrc_t dr = row_rsrc(x_perm + (size_t)r * nvec, row_bytes);
+#pragma unroll
+      for (int u = 0; u < kGatherVec; ++u) {
+        const int v = v0 + u * blockDim.x;
+        int32x4_t o = val[u];
+        if constexpr (SCALED) o = scale_row(o, ws[k], (const ET*)nullptr);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            o, dr, v < nvec ? (uint32_t)v * 16u : row_bytes, 0, kNonTemporal);
+      }
+    }
+  }
 }
 
 template <typename ET>
@@ -260,14 +310,7 @@ __global__ __launch_bounds__(256) void gather_scaled_kernel(const uint4* __restr
     ws[threadIdx.x] = pair_w[(size_t)t * K + threadIdx.x];
   }
   __syncthreads();
-  const uint4* src = x + (size_t)t * nvec;
-  for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
-    const uint4 val = src[v];
-    for (int k = 0; k < K; ++k) {
-      const int r = rows[k];
-      if (r >= 0) x_perm[(size_t)r * nvec + v] = scale_row(val, ws[k], (const ET*)nullptr);
-    }
-  }
+  gather_rows<true, ET>(x + (size_t)t * nvec, nvec, K, rows, ws, x_perm);
 }
 
 }  // namespace
