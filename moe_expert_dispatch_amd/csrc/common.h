@@ -80,6 +80,49 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// The same reductions over aligned groups of L = 8, 16 or 32 lanes (the
+// first steps only; groups never exchange values): every lane of a group
+// ends with the group's result, bit-identical across the group.
+template <int L>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+  static_assert(L == 8 || L == 16 || L == 32, "groups of 8, 16 or 32 lanes");
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  v = mx(v, dpp_u32<kDppQuad1032>(v));
+  v = mx(v, dpp_u32<kDppQuad2301>(v));
+  v = mx(v, dpp_u32<kDppRowHalfMirror>(v));
+  if constexpr (L >= 16) v = mx(v, dpp_u32<kDppRowMirror>(v));
+  if constexpr (L == 32) {
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = mx(a[0], a[1]);
+  }
+  return v;
+}
+
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(L == 8 || L == 16 || L == 32, "groups of 8, 16 or 32 lanes");
+  auto dpp = [](float x, auto ctrl) {
+    return __uint_as_float(dpp_u32<decltype(ctrl)::value>(__float_as_uint(x)));
+  };
+  v += dpp(v, std::integral_constant<int, kDppQuad1032>{});
+  v += dpp(v, std::integral_constant<int, kDppQuad2301>{});
+  v += dpp(v, std::integral_constant<int, kDppRowHalfMirror>{});
+  if constexpr (L >= 16) v += dpp(v, std::integral_constant<int, kDppRowMirror>{});
+  if constexpr (L == 32) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  }
+  return v;
+}
+
+template <int L>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
+  const uint32_t hi = group_max_u32<L>((uint32_t)(v >> 32));
+  const uint32_t lo = group_max_u32<L>((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // 64-bit maximum as two 32-bit passes: the high words, then the low words of
 // the lanes holding that high word.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
@@ -90,6 +133,38 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 
 // ---------------------------------------------------------------- misc
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Expert-parallel mask / remap and expert -> slot lookup of one pair p =
+// t * K + k with expert e and routing weight wv (vLLM ep_fused_moe_patch.py,
+// ep_mask_and_remap: local mask for the rank's range [start, start + E_local),
+// weight times the mask, local id e - start, non-local ids spread by
+// e mod E_local; TensorRT-LLM PR #4495: expert id -> engine-side slot). The
+// replica of a local expert is chosen by token index, t mod r. A null table
+// is the identity map; an entry outside [0, S) (or an expert without slots)
+// gives slot -1.
+__device__ __forceinline__ void map_pair(int p, int t, int e, float wv, int start, int E_local,
+                                         const int32_t* __restrict__ rep_off,
+                                         const int32_t* __restrict__ rep_slots, int S,
+                                         int32_t* __restrict__ slot,
+                                         float* __restrict__ w_masked,
+                                         uint8_t* __restrict__ mask) {
+  const bool local = e >= start && e < start + E_local;
+  const int lid = local ? e - start : ((e % E_local) + E_local) % E_local;
+  int s = lid;
+  if (rep_off != nullptr) {
+    const int a = rep_off[lid];
+    const int b = rep_off[lid + 1];
+    const int r = b - a;
+    s = -1;
+    if (r > 0 && a >= 0 && b <= S) {
+      const int v = rep_slots[a + t % r];
+      s = (v >= 0 && v < S) ? v : -1;
+    }
+  }
+  slot[p] = s;
+  w_masked[p] = wv * (local ? 1.0f : 0.0f);
+  mask[p] = local ? 1 : 0;
+}
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -105,6 +180,13 @@ int device_cu_count();
 // G == 0: plain top-K; else group-limited routing over G groups keeping TG.
 moe_status_t launch_route(const float* logits, int T, int E, int K, int renorm, int G, int TG,
                           int32_t* ids, float* w, hipStream_t stream);
+// launch_route followed by launch_slot_map, as one kernel where the router
+// runs with lane groups (the same bits as the two calls).
+moe_status_t launch_route_map(const float* logits, int T, int E, int K, int renorm, int G,
+                              int TG, int32_t* ids, float* w, int start, int E_local,
+                              const int32_t* rep_off, const int32_t* rep_slots, int S,
+                              int32_t* slot, float* w_masked, uint8_t* mask,
+                              hipStream_t stream);
 moe_status_t launch_slot_map(const int32_t* ids, const float* w, int T, int K, int start,
                              int E_local, const int32_t* rep_off, const int32_t* rep_slots,
                              int S, int32_t* slot, float* w_masked, uint8_t* mask,

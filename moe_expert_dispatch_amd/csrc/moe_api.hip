@@ -375,13 +375,14 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_forward_args_t* args
   const int32_t* ids_in = args->topk_ids;
   const float* w_in = args->topk_w;
   if (args->logits) {
-    MOE_TRY(launch_route(args->logits, T, cfg->E_global, K, cfg->renormalize ? 1 : 0,
-                         cfg->num_expert_group, cfg->topk_group, ids, w, stream));
-    ids_in = ids;
-    w_in = w;
+    MOE_TRY(launch_route_map(args->logits, T, cfg->E_global, K, cfg->renormalize ? 1 : 0,
+                             cfg->num_expert_group, cfg->topk_group, ids, w,
+                             cfg->ep_rank * E_local, E_local, args->rep_off, args->rep_slots, S,
+                             slot, w_masked, mask, stream));
+  } else {
+    MOE_TRY(launch_slot_map(ids_in, w_in, T, K, cfg->ep_rank * E_local, E_local, args->rep_off,
+                            args->rep_slots, S, slot, w_masked, mask, stream));
   }
-  MOE_TRY(launch_slot_map(ids_in, w_in, T, K, cfg->ep_rank * E_local, E_local, args->rep_off,
-                          args->rep_slots, S, slot, w_masked, mask, stream));
   MOE_TRY(mark(MOE_EV_ROUTED));
   // bf16 with a direct-to-LDS shape: the gate/up GEMM fetches token rows of x
   // itself, so the permutation only orders the pairs (no x_perm copy).

@@ -12,6 +12,15 @@
 // the largest logit and, among equal logits, the lowest id. K rounds of a
 // wave-wide max select the experts; the winner's owner lane clears its key.
 //
+// Up to 256 experts (K <= 8 or the lane count, no groups) a token gets
+// L = 8, 16 or 32 lanes of a wave (at most 8 logits per lane) instead of a
+// whole wave: lane q holds experts q, q + L, ..., and each
+// round's maximum is a per-lane maximum followed by DPP steps inside the
+// group (route_lanes_kernel). Both forms give the same ids; the weights are
+// the same softmax with the sums taken in a different order, and moe_route,
+// moe_forward and the fused route + slot map of moe_forward all take the
+// same form for a given shape, so their bits agree.
+//
 // Group-limited routing (the constructor's use_grouped_topk,
 // num_expert_group and topk_group, which the pages only name; reading: the
 // E experts form G consecutive groups scored by their largest logit): lane g
@@ -30,6 +39,94 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+
+// Inverse of ordered_bits for non-NaN keys (-0.0 comes back as +0.0, which
+// gives the same exponentials).
+__device__ __forceinline__ float from_ordered(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+// Where the fused router writes the slot map (null slot: route only).
+struct MapOut {
+  int start, E_local, S;
+  const int32_t* rep_off;
+  const int32_t* rep_slots;
+  int32_t* slot;
+  float* w_masked;
+  uint8_t* mask;
+};
+
+// L lanes per token, EPL logits per lane (a power of two); K <= L,
+// E <= L * EPL. Lanes of
+// tokens past T carry empty keys and store nothing, but stay active, so every
+// DPP step reads live lanes.
+template <int L, int EPL, bool MAP>
+__global__ __launch_bounds__(256) void route_lanes_kernel(const float* __restrict__ logits,
+                                                          int T, int E, int K, int renorm,
+                                                          int32_t* __restrict__ ids,
+                                                          float* __restrict__ w, MapOut mo) {
+  const int q = threadIdx.x & (L - 1);
+  const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) / L);
+  const bool live = t < T;
+  const float* row = logits + (size_t)(live ? t : 0) * E;
+
+  float v[EPL];
+  uint64_t key[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = q + L * j;
+    if (live && e < E) {
+      v[j] = row[e];
+      key[j] = ((uint64_t)ordered_bits(v[j]) << 32) | (0xffffffffu - (uint32_t)e);
+    } else {
+      v[j] = -INFINITY;
+      key[j] = 0;
+    }
+  }
+
+  // K rounds; lane k of the group keeps the k-th selection's key.
+  uint64_t my_key = 0;
+  uint64_t top = 0;
+  for (int k = 0; k < K; ++k) {
+    // the lane's maximum as a tree (depth log2 EPL rather than EPL - 1)
+    uint64_t b[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) b[j] = key[j];
+#pragma unroll
+    for (int h = EPL / 2; h >= 1; h /= 2)
+#pragma unroll
+      for (int j = 0; j < h; ++j) b[j] = b[j + h] > b[j] ? b[j + h] : b[j];
+    const uint64_t best = group_max_u64<L>(b[0]);
+    const int e = (int)(0xffffffffu - (uint32_t)best);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (q + L * j == e) key[j] = 0;
+    if (q == k) my_key = best;
+    if (k == 0) top = best;
+  }
+
+  // Softmax with the top logit as the shift.
+  const float m = from_ordered((uint32_t)(top >> 32));
+  float part = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j)
+    if (q + L * j < E) part += expf(v[j] - m);
+  const float denom = group_sum<L>(part);
+  float p = (q < K) ? expf(from_ordered((uint32_t)(my_key >> 32)) - m) / denom : 0.f;
+  if (renorm) {
+    const float s = group_sum<L>(p);
+    p = p / s;
+  }
+  if (live && q < K) {
+    const int id = (int)(0xffffffffu - (uint32_t)my_key);
+    const int pi = t * K + q;
+    ids[pi] = id;
+    w[pi] = p;
+    if constexpr (MAP)
+      map_pair(pi, t, id, p, mo.start, mo.E_local, mo.rep_off, mo.rep_slots, mo.S, mo.slot,
+               mo.w_masked, mo.mask);
+  }
+}
 
 // G == 0: plain top-K over all experts; otherwise 1 <= TG <= G <= 64, E % G == 0.
 template <int EPL>
@@ -122,11 +219,69 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   }
 }
 
+// Lanes per token for the grouped-lane router (at most 8 logits per lane and
+// K <= L), or 0 where the wave-per-token kernel runs (group-limited routing,
+// more than 256 experts, K > 32).
+int lanes_for(int E, int K, int G) {
+  if (G != 0 || E > 256 || K > 32) return 0;
+  if (E <= 64 && K <= 8) return 8;
+  if (E <= 128 && K <= 16) return 16;
+  return 32;
+}
+
+template <int L, bool MAP>
+void launch_lanes(const float* logits, int T, int E, int K, int renorm, int32_t* ids, float* w,
+                  const MapOut& mo, hipStream_t stream) {
+  const int epl = ceil_div(E, L);
+  const dim3 grid((unsigned)ceil_div(T, 256 / L));
+  if (epl <= 1)
+    route_lanes_kernel<L, 1, MAP><<<grid, 256, 0, stream>>>(logits, T, E, K, renorm, ids, w, mo);
+  else if (epl <= 2)
+    route_lanes_kernel<L, 2, MAP><<<grid, 256, 0, stream>>>(logits, T, E, K, renorm, ids, w, mo);
+  else if (epl <= 4)
+    route_lanes_kernel<L, 4, MAP><<<grid, 256, 0, stream>>>(logits, T, E, K, renorm, ids, w, mo);
+  else
+    route_lanes_kernel<L, 8, MAP><<<grid, 256, 0, stream>>>(logits, T, E, K, renorm, ids, w, mo);
+}
+
+template <bool MAP>
+void launch_lanes_any(int L, const float* logits, int T, int E, int K, int renorm, int32_t* ids,
+                      float* w, const MapOut& mo, hipStream_t stream) {
+  if (L == 8)
+    launch_lanes<8, MAP>(logits, T, E, K, renorm, ids, w, mo, stream);
+  else if (L == 16)
+    launch_lanes<16, MAP>(logits, T, E, K, renorm, ids, w, mo, stream);
+  else
+    launch_lanes<32, MAP>(logits, T, E, K, renorm, ids, w, mo, stream);
+}
+
 }  // namespace
+
+moe_status_t launch_route_map(const float* logits, int T, int E, int K, int renorm, int G,
+                              int TG, int32_t* ids, float* w, int start, int E_local,
+                              const int32_t* rep_off, const int32_t* rep_slots, int S,
+                              int32_t* slot, float* w_masked, uint8_t* mask,
+                              hipStream_t stream) {
+  if (T == 0) return MOE_OK;
+  const int L = lanes_for(E, K, G);
+  if (L == 0) {
+    const moe_status_t st = launch_route(logits, T, E, K, renorm, G, TG, ids, w, stream);
+    if (st != MOE_OK) return st;
+    return launch_slot_map(ids, w, T, K, start, E_local, rep_off, rep_slots, S, slot, w_masked,
+                           mask, stream);
+  }
+  const MapOut mo{start, E_local, S, rep_off, rep_slots, slot, w_masked, mask};
+  launch_lanes_any<true>(L, logits, T, E, K, renorm, ids, w, mo, stream);
+  return launch_status();
+}
 
 moe_status_t launch_route(const float* logits, int T, int E, int K, int renorm, int G, int TG,
                           int32_t* ids, float* w, hipStream_t stream) {
   if (T == 0) return MOE_OK;
+  if (const int L = lanes_for(E, K, G)) {
+    launch_lanes_any<false>(L, logits, T, E, K, renorm, ids, w, MapOut{}, stream);
+    return launch_status();
+  }
   const dim3 block(256);
   const dim3 grid(ceil_div(T, 256 / kWave));
   const int epl = ceil_div(E, kWave);

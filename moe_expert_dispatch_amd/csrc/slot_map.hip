@@ -1,5 +1,6 @@
 // Expert-parallel mask / remap and expert -> slot lookup, one thread per
-// (token, k) pair.
+// (token, k) pair (the per-pair rule is map_pair in common.h, which the fused
+// router of moe_forward applies too).
 //
 // Source: vLLM ep_fused_moe_patch.py, ep_mask_and_remap (local mask for the
 // rank's expert range, weights multiplied by the mask, local id = id - start,
@@ -18,24 +19,7 @@ __global__ __launch_bounds__(256) void slot_map_kernel(
     uint8_t* __restrict__ mask) {
   const int p = blockIdx.x * blockDim.x + threadIdx.x;
   if (p >= P) return;
-  const int t = p / K;
-  const int e = ids[p];
-  const bool local = e >= start && e < start + E_local;
-  const int lid = local ? e - start : ((e % E_local) + E_local) % E_local;
-  int s = lid;
-  if (rep_off != nullptr) {
-    const int a = rep_off[lid];
-    const int b = rep_off[lid + 1];
-    const int r = b - a;
-    s = -1;
-    if (r > 0 && a >= 0 && b <= S) {
-      const int v = rep_slots[a + t % r];
-      s = (v >= 0 && v < S) ? v : -1;
-    }
-  }
-  slot[p] = s;
-  w_masked[p] = w[p] * (local ? 1.0f : 0.0f);
-  mask[p] = local ? 1 : 0;
+  map_pair(p, p / K, ids[p], w[p], start, E_local, rep_off, rep_slots, S, slot, w_masked, mask);
 }
 
 }  // namespace
