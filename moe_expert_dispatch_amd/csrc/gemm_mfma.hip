@@ -560,8 +560,11 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
   };
   // DMA instruction q (0..7) of slice d into buffer d & 1: 8 rows x 128
   // bytes, i.e. whole cache lines.
-  auto dma = [&](const WItem& x, int q, int d) {
-    const bool live = d < nd;
+  // `chk` false: the caller knows d < nd. An out-of-range row or column
+  // offset (kOOB) stays out of range with the slice offset added (every
+  // resource is under 2 GiB), so it needs no test of its own.
+  auto dma = [&](const WItem& x, int q, int d, bool chk = true) {
+    const bool live = !chk || d < nd;
     const uint32_t kb = (uint32_t)d * (WBK * 2);
     uint4* stage = smem + (d & 1) * WSTAGE_VEC;
     if (q < 4) {
@@ -572,7 +575,7 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
       const int i = q - 4;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           x.rb, (lds_ptr_t)(stage + WA_VEC + (wave * 4 + i) * 64), 16,
-          (live && x.b_off[i] != kOOB) ? x.b_off[i] + kb : kOOB, 0, 0, 0);
+          live ? x.b_off[i] + kb : kOOB, 0, 0, 0);
     }
   };
   auto issue_slice = [&](const WItem& x, int d) {
@@ -778,7 +781,7 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
   // waited for and the workgroup synchronises, after which slice d+1 is
   // visible everywhere and buffer d & 1 is no longer read, so the DMA of
   // slice d+2 goes there while block 0 of slice d+1 is read.
-  auto dstep = [&](int d, auto first) {
+  auto dstep = [&](int d, auto first, auto chk) {
     const uint32_t base = smem_base + (uint32_t)(d & 1) * WSTAGE_BYTES;
     const uint32_t nbase = smem_base + (uint32_t)((d + 1) & 1) * WSTAGE_BYTES;
     wait_frags(f0a, f0b);
@@ -810,7 +813,7 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-      dma(cur, x, d + 2);
+      dma(cur, x, d + 2, decltype(chk)::value);
       if (x < 6) read8(x, f0a, f0b, nbase + a_lane[0], nbase + b_lane[0]);
       mfma1(x, f1a, f1b);
       __builtin_amdgcn_sched_barrier(0);
@@ -975,11 +978,16 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
 #pragma unroll
         for (int x = 0; x < 6; ++x)
           read8(x, f0a, f0b, smem_base + a_lane[0], smem_base + b_lane[0]);
-        dstep(0, std::true_type{});
-        for (int d = 1; d < dlast; ++d) dstep(d, std::false_type{});
+        const std::true_type checked;
+        const std::false_type unchecked;
+        dstep(0, std::true_type{}, checked);
+        // the DMA of slice d + 2 is in range for d < nd - 2
+        int d = 1;
+        for (; d < dlast && d < nd - 2; ++d) dstep(d, std::false_type{}, unchecked);
+        for (; d < dlast; ++d) dstep(d, std::false_type{}, checked);
         if constexpr (GATHER) {
           next_setup();
-          dstep(nd - 1, std::false_type{});
+          dstep(nd - 1, std::false_type{}, checked);
         }
         vm_wait<0>();
         wait_frags(f0a, f0b);
