@@ -13,6 +13,8 @@
 // f32 in ascending k with fused multiply-adds and writes the token's output
 // row once. Every output element is written by exactly one thread, so the
 // result does not depend on scheduling.
+#include <algorithm>
+
 #include "common.h"
 
 namespace moe {
@@ -174,9 +176,13 @@ template <typename YT, typename OT>
 void launch_typed(const void* y, const int32_t* pair_row, const float* w_masked, int T, int K,
                   int H, void* out, int accumulate, const void* shared, int shared_bf16,
                   hipStream_t stream) {
-  combine_kernel<YT, OT, 8><<<T, 256, 0, stream>>>(static_cast<const YT*>(y), pair_row, w_masked,
-                                                   K, H, static_cast<OT*>(out), accumulate,
-                                                   shared, shared_bf16);
+  // kVec vectors of 8 elements per thread: H / 16 threads, whole waves,
+  // at most 256 (wider rows loop), so narrow rows leave no thread idle and
+  // more tokens fit on a CU.
+  const int threads = std::min(256, std::max(kWave, ceil_div(H / 8, kVec * kWave) * kWave));
+  combine_kernel<YT, OT, 8><<<T, threads, 0, stream>>>(static_cast<const YT*>(y), pair_row,
+                                                       w_masked, K, H, static_cast<OT*>(out),
+                                                       accumulate, shared, shared_bf16);
 }
 
 }  // namespace
