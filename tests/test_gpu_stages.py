@@ -52,11 +52,20 @@ def _route_case(name):
         return torch.randn(100, 64, generator=g) * 40, 8, True
     if name == "t0":
         return torch.zeros(0, 8), 2, True
+    # lane-group router forms: 32 lanes per token with K > 16, K = 32 lanes at
+    # 256 experts, and a token count that leaves a partial block of 32-lane
+    # groups (with tied logits)
+    if name == "l32_k24":
+        return torch.randn(90, 40, generator=g), 24, True
+    if name == "e256_k32":
+        return torch.randn(64, 256, generator=g) * 2, 32, False
+    if name == "e200_ragged_ties":
+        return torch.round(torch.randn(77, 200, generator=g) * 3) / 3, 7, True
     raise KeyError(name)
 
 
 ROUTE_CASES = list(CONFIGS) + ["ties", "k_eq_e", "max_e_k", "e1", "e65_ragged", "zeros_equal",
-                               "wide_range", "t0"]
+                               "wide_range", "t0", "l32_k24", "e256_k32", "e200_ragged_ties"]
 
 
 @pytest.mark.parametrize("name", ROUTE_CASES)
