@@ -175,6 +175,76 @@ inline moe_status_t launch_status() {
 // Number of compute units of the current device (queried once per device).
 int device_cu_count();
 
+// ---------------------------------------------------------------- FP8
+// Quantization to OCP E4M3 with one scale per tensor: code = E4M3 value
+// nearest to clamp(x * (1 / scale), -448, 448), ties to the even code.
+// v_cvt_pk_fp8_f32 rounds to nearest even but turns magnitudes past the
+// 448 / 480 midpoint into NaN, so every value is clamped first.
+typedef int fp8_i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float fp8_clamp448(float v) {
+  return fminf(fmaxf(v, -448.0f), 448.0f);
+}
+
+// four values -> four codes, first value in the lowest byte
+__device__ __forceinline__ uint32_t fp8_q4(float a, float b, float c, float d, float inv) {
+  const int lo =
+      __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp448(a * inv), fp8_clamp448(b * inv), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp448(c * inv),
+                                                   fp8_clamp448(d * inv), lo, true);
+}
+
+__device__ __forceinline__ float fp8_ld(const uint16_t* x, int64_t i) {
+  return bf16_to_f32(x[i]);
+}
+__device__ __forceinline__ float fp8_ld(const float* x, int64_t i) { return x[i]; }
+
+// 16 values per thread: 16-byte loads and one 16-byte store; the last
+// partial group (n % 16) element by element.
+__device__ __forceinline__ void fp8_load16(const uint16_t* x, int64_t i0, float* v) {
+  const fp8_i32x4_t* p = reinterpret_cast<const fp8_i32x4_t*>(x + i0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const fp8_i32x4_t w = p[h];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[8 * h + 2 * k] = bf16_to_f32((uint32_t)w[k] & 0xffffu);
+      v[8 * h + 2 * k + 1] = bf16_to_f32((uint32_t)w[k] >> 16);
+    }
+  }
+}
+__device__ __forceinline__ void fp8_load16(const float* x, int64_t i0, float* v) {
+  const float4* p = reinterpret_cast<const float4*>(x + i0);
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const float4 w = p[h];
+    v[4 * h] = w.x;
+    v[4 * h + 1] = w.y;
+    v[4 * h + 2] = w.z;
+    v[4 * h + 3] = w.w;
+  }
+}
+
+// Thread g of a quantization of n values: values [16 g, 16 g + 16).
+template <typename XT>
+__device__ __forceinline__ void quantize16(const XT* __restrict__ x, int64_t n, float inv,
+                                           uint8_t* __restrict__ q, int64_t g) {
+  const int64_t i0 = g * 16;
+  if (i0 >= n) return;
+  if (i0 + 16 <= n) {
+    float v[16];
+    fp8_load16(x, i0, v);
+    fp8_i32x4_t out;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      out[k] = (int)fp8_q4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3], inv);
+    *reinterpret_cast<fp8_i32x4_t*>(q + i0) = out;
+  } else {
+    for (int64_t i = i0; i < n; ++i)
+      q[i] = (uint8_t)(fp8_q4(fp8_ld(x, i), 0.0f, 0.0f, 0.0f, inv) & 0xffu);
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 // Host-side launchers; arguments are validated by the C-ABI layer.
 // G == 0: plain top-K; else group-limited routing over G groups keeping TG.
@@ -192,6 +262,15 @@ moe_status_t launch_slot_map(const int32_t* ids, const float* w, int T, int K, i
                              int S, int32_t* slot, float* w_masked, uint8_t* mask,
                              hipStream_t stream);
 
+// Quantization of a bf16 tensor of n values to E4M3 codes (scale 1 / inv),
+// run as extra blocks of the permutation's scatter launch (independent work).
+struct FusedQuant {
+  const uint16_t* x;
+  int64_t n;
+  float inv;
+  uint8_t* q;
+};
+
 struct PermutePlan {
   int P;        // pairs
   int chunk;    // pairs per chunk (multiple of 256)
@@ -202,11 +281,12 @@ PermutePlan permute_plan(int T, int K, int S);
 // seg_cap > 0 places slot s's rows in the fixed block [s * seg_cap,
 // (s + 1) * seg_cap) (the caller guarantees every slot fits). pair_w non-null:
 // the row of pair p is pair_w[p] * x[p / K] (f32 product, rounded once).
+// quant non-null: its quantization runs as extra blocks of the scatter launch.
 moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
                             const int32_t* slot, const uint8_t* mask, int S, int32_t* offsets,
                             int32_t* sorted_pairs, int32_t* pair_row, void* x_perm, void* ws,
                             hipStream_t stream, int seg_cap = 0,
-                            const float* pair_w = nullptr);
+                            const float* pair_w = nullptr, const FusedQuant* quant = nullptr);
 
 moe_status_t launch_gemm_bf16(moe_gemm_op_t op, const void* a, const int32_t* offsets, int S,
                               int max_rows, const void* w, int H, int I, void* c,

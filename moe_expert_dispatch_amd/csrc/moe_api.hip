@@ -391,10 +391,13 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_forward_args_t* args
   // FP8: x is quantized once per token and GEMM 1 gathers the code rows.
   const bool fused_gather =
       fp8 || (!on_input && cfg->dtype == MOE_DTYPE_BF16 && gemm_bf16_gather_ok(T, H));
-  if (fp8) MOE_TRY(launch_quantize_fp8(args->x, true, (int64_t)T * H, cfg->a1_scale, xq, stream));
+  // FP8: x is quantized by extra blocks of the permutation's scatter launch
+  const FusedQuant fq{static_cast<const uint16_t*>(args->x), (int64_t)T * H,
+                      1.0f / cfg->a1_scale, xq};
   MOE_TRY(launch_permute(args->x, fp8 ? 2 : dtype_bytes(cfg->dtype), T, H, K, slot, mask, S,
                          offsets, sorted_pairs, pair_row, fused_gather ? nullptr : x_perm,
-                         perm_ws, stream, 0, on_input ? w_masked : nullptr));
+                         perm_ws, stream, 0, on_input ? w_masked : nullptr,
+                         fp8 ? &fq : nullptr));
   MOE_TRY(mark(MOE_EV_PERMUTED));
   if (fp8)
     MOE_TRY(launch_gemm_fp8_gate_up_gathered(

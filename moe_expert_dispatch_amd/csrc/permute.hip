@@ -141,18 +141,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict_
 // base row, so the order inside a slot is the pair order.
 // seg_cap > 0: slot s's rows start at s * seg_cap instead of offsets[s]
 // (fixed-capacity blocks, one per slot).
-__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ slot,
-                                                      const uint8_t* __restrict__ mask, int P,
-                                                      int S, int chunk, int nchunks,
-                                                      const int32_t* __restrict__ base,
-                                                      const int32_t* __restrict__ offsets,
-                                                      int seg_cap,
-                                                      int32_t* __restrict__ sorted_pairs,
-                                                      int32_t* __restrict__ pair_row) {
+__device__ __forceinline__ void scatter_chunk(int c, const int32_t* __restrict__ slot,
+                                              const uint8_t* __restrict__ mask, int P, int S,
+                                              int chunk, int nchunks,
+                                              const int32_t* __restrict__ base,
+                                              const int32_t* __restrict__ offsets, int seg_cap,
+                                              int32_t* __restrict__ sorted_pairs,
+                                              int32_t* __restrict__ pair_row) {
   extern __shared__ int32_t lds[];
   int32_t* running = lds;       // [S] next free row per slot
   int32_t* bcount = lds + S;    // [kBatches][S] counts, then base rows
-  const int c = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
@@ -209,6 +207,36 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
     }
     __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ slot,
+                                                      const uint8_t* __restrict__ mask, int P,
+                                                      int S, int chunk, int nchunks,
+                                                      const int32_t* __restrict__ base,
+                                                      const int32_t* __restrict__ offsets,
+                                                      int seg_cap,
+                                                      int32_t* __restrict__ sorted_pairs,
+                                                      int32_t* __restrict__ pair_row) {
+  scatter_chunk(blockIdx.x, slot, mask, P, S, chunk, nchunks, base, offsets, seg_cap,
+                sorted_pairs, pair_row);
+}
+
+// The scatter with a quantization riding along: blocks [0, nchunks) scatter
+// their chunk, the remaining blocks quantize 16 values per thread. The two
+// are independent, so the quantization's HBM traffic overlaps the
+// latency-bound scatter instead of following it. The branch is uniform per
+// block, so the scatter's barriers are reached by whole blocks.
+__global__ __launch_bounds__(256) void scatter_quant_kernel(
+    const int32_t* __restrict__ slot, const uint8_t* __restrict__ mask, int P, int S, int chunk,
+    int nchunks, const int32_t* __restrict__ base, const int32_t* __restrict__ offsets,
+    int seg_cap, int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_row,
+    FusedQuant fq) {
+  if ((int)blockIdx.x < nchunks)
+    scatter_chunk(blockIdx.x, slot, mask, P, S, chunk, nchunks, base, offsets, seg_cap,
+                  sorted_pairs, pair_row);
+  else
+    quantize16(fq.x, fq.n, fq.inv, fq.q,
+               (int64_t)(blockIdx.x - (unsigned)nchunks) * blockDim.x + threadIdx.x);
 }
 
 typedef int int32x4_t __attribute__((ext_vector_type(4)));
@@ -334,7 +362,8 @@ PermutePlan permute_plan(int T, int K, int S) {
 moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
                             const int32_t* slot, const uint8_t* mask, int S, int32_t* offsets,
                             int32_t* sorted_pairs, int32_t* pair_row, void* x_perm, void* ws,
-                            hipStream_t stream, int seg_cap, const float* pair_w) {
+                            hipStream_t stream, int seg_cap, const float* pair_w,
+                            const FusedQuant* quant) {
   const PermutePlan pl = permute_plan(T, K, S);
   // the one-pass scan covers up to 64 entries per thread
   if ((long long)S * pl.nchunks > (long long)kScanThreads * 4 * kScanVec)
@@ -346,11 +375,18 @@ moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
                                                   hist);
   }
   scan_kernel<<<1, kScanThreads, 0, stream>>>(hist, S, pl.nchunks, offsets);
-  if (pl.nchunks > 0) {
+  const int64_t qblocks =
+      (quant != nullptr && quant->n > 0) ? ((quant->n + 15) / 16 + 255) / 256 : 0;
+  if (pl.nchunks > 0 || qblocks > 0) {
     const size_t lds_scatter = (size_t)(1 + kBatches) * S * sizeof(int32_t);
-    scatter_kernel<<<pl.nchunks, 256, lds_scatter, stream>>>(slot, mask, pl.P, S, pl.chunk,
-                                                            pl.nchunks, hist, offsets, seg_cap,
-                                                            sorted_pairs, pair_row);
+    if (qblocks > 0)
+      scatter_quant_kernel<<<(unsigned)(pl.nchunks + qblocks), 256, lds_scatter, stream>>>(
+          slot, mask, pl.P, S, pl.chunk, pl.nchunks, hist, offsets, seg_cap, sorted_pairs,
+          pair_row, *quant);
+    else
+      scatter_kernel<<<pl.nchunks, 256, lds_scatter, stream>>>(slot, mask, pl.P, S, pl.chunk,
+                                                              pl.nchunks, hist, offsets,
+                                                              seg_cap, sorted_pairs, pair_row);
   }
   if (x_perm != nullptr && T > 0) {
     const int nvec = H * elem_bytes / 16;
