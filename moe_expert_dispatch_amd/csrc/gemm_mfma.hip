@@ -44,9 +44,10 @@
 // r*G + (b mod 8)*(G/8) + b/8. Blocks b, b+8, ... run on the same XCD (the
 // dispatcher deals workgroups to the 8 XCDs round-robin), so each XCD works
 // on a contiguous run of 32 items per round. Items are numbered in groups of
-// GM row tiles x GN column tiles (GN = min(column tiles, 8), GM = 32 / GN),
+// GM row tiles x GN column tiles (GN = min(column tiles, 4), GM = 32 / GN),
 // so one XCD's 32 concurrent items share GM activation tiles and GN weight
-// panels in its L2.
+// panels in its L2; partial groups at the row and column ends are numbered
+// without holes (item_tile).
 #include <type_traits>
 
 #include "common.h"
@@ -62,6 +63,7 @@ constexpr int BK = 64;
 constexpr int BROWS = 256;  // weight rows per stage
 constexpr int NTHR = 256;
 constexpr int XCD_ITEMS = 32;  // concurrent items per XCD per round
+constexpr int kGroupCols = 4;  // column tiles per item group (8 row tiles x 4)
 constexpr int A_VEC = BM * BK / 8;     // 16-byte vectors per A stage (1024)
 constexpr int B_VEC = BROWS * BK / 8;  // 2048
 constexpr int STAGE_VEC = A_VEC + B_VEC;
@@ -125,19 +127,28 @@ __device__ __forceinline__ int find_slot(const int32_t* tp, int S, int rt) {
   return lo;
 }
 
-// Maps item w to (row tile, column tile) in GM x GN groups; false for the
-// holes of partial groups.
-__device__ __forceinline__ bool item_tile(int w, int RT, int CT, int GM, int GN, int* rt,
-                                          int* ct) {
-  const int per = GM * GN;
-  const int group = w / per;
-  const int within = w - group * per;
-  const int ncg = ceil_div(CT, GN);
-  const int rg = group / ncg;
-  const int cg = group - rg * ncg;
-  *rt = rg * GM + within / GN;
-  *ct = cg * GN + within % GN;
-  return *rt < RT && *ct < CT;
+// Maps item w in [0, RT * CT) to (row tile, column tile). Items run through
+// groups of GM row tiles x GN column tiles (row groups outermost); the last
+// row group and the last column group of each row group take only the tiles
+// that exist, so the numbering has no holes: with a static item-to-block
+// assignment a hole would cost a block a whole item's time.
+__host__ __device__ __forceinline__ void item_tile(int w, int RT, int CT, int GM, int GN,
+                                                   int* rt, int* ct) {
+  const int rg = w / (GM * CT);               // row group
+  const int h = min(GM, RT - rg * GM);        // its height
+  const int v = w - rg * GM * CT;             // item inside the row group
+  const int full = CT / GN;                   // whole column groups
+  if (v < full * h * GN) {
+    const int cg = v / (h * GN);
+    const int within = v - cg * h * GN;
+    *rt = rg * GM + within / GN;
+    *ct = cg * GN + within % GN;
+  } else {                                    // the last, narrower column group
+    const int r = CT - full * GN;
+    const int u = v - full * h * GN;
+    *rt = rg * GM + u / r;
+    *ct = full * GN + u % r;
+  }
 }
 
 // OP 0: gate/up + SwiGLU (Kd = H, N = I, weight rows per slot 2I).
@@ -159,13 +170,13 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_kernel(
   const size_t w_rows = (OP == 0) ? 2 * (size_t)N : (size_t)N;
   const int BN = (OP == 0) ? BROWS / 2 : BROWS;  // output columns per tile
   const int CT = ceil_div(N, BN);
-  const int GN = CT < 8 ? CT : 8;
+  const int GN = CT < kGroupCols ? CT : kGroupCols;
   const int GM = XCD_ITEMS / GN;
   const int nk = ceil_div(Kd, BK);
 
   build_tile_prefix<NTHR>(offsets, S, tp, scan_scratch);
   const int RT = uniform(tp[S]);
-  const int total = ceil_div(RT, GM) * GM * ceil_div(CT, GN) * GN;
+  const int total = RT * CT;
 
   const int G = gridDim.x;
   const int b = blockIdx.x;
@@ -173,7 +184,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_kernel(
 
   for (int item = first; item < total; item += G) {
     int rt, ct;
-    if (!item_tile(item, RT, CT, GM, GN, &rt, &ct)) continue;  // block-uniform
+    item_tile(item, RT, CT, GM, GN, &rt, &ct);
     const int s = uniform(find_slot(tp, S, rt));
     const int row0 = uniform(offsets[s] + (rt - tp[s]) * BM);
     const int rows = uniform(min(BM, offsets[s + 1] - row0));
@@ -470,7 +481,7 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
   const size_t w_rows = (OP == 0) ? 2 * (size_t)N : (size_t)N;
   const int BN = (OP == 0) ? BROWS / 2 : BROWS;
   const int CT = ceil_div(N, BN);
-  const int GN = CT < 8 ? CT : 8;
+  const int GN = CT < kGroupCols ? CT : kGroupCols;
   const int GM = XCD_ITEMS / GN;
   constexpr int EB = FP8 ? 1 : 2;                       // operand bytes (A and W are uint4*)
   constexpr uint32_t OB = (FP8 && OP == 0) ? 1u : 2u;   // output bytes
@@ -479,7 +490,7 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
 
   build_tile_prefix<NTHR8>(offsets, S, tp, scan_scratch);
   const int RT = uniform(tp[S]);
-  const int total = ceil_div(RT, GM) * GM * ceil_div(CT, GN) * GN;
+  const int total = RT * CT;
   const int G = gridDim.x;
   const int b = blockIdx.x;
 
@@ -501,7 +512,7 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
   const __amdgpu_buffer_rsrc_t g_rsrc =
       make_rsrc(gather, GATHER ? (uint32_t)a_rows * (uint32_t)topk * 4u : 0u);
   auto next_item = [&](int w, int* rt, int* ct) {
-    while (w < total && !item_tile(w, RT, CT, GM, GN, rt, ct)) w += G;
+    if (w < total) item_tile(w, RT, CT, GM, GN, rt, ct);
     return w;
   };
   auto setup = [&](int rt, int ct, WItem& x) {
