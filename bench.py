@@ -35,7 +35,9 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_F32_TFLOPS = 157.3  # MI355X fp32 vector (FMA) peak
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")  # <workload>_gate_up_traffic.json
-GEMM_SRC = os.path.join(ROOT, "moe_expert_dispatch_amd", "csrc", "gemm_mfma.hip")
+# the GEMM kernels and the item order they share
+GEMM_SRC = [os.path.join(ROOT, "moe_expert_dispatch_amd", "csrc", f)
+            for f in ("gemm_mfma.hip", "item_order.h")]
 
 
 def parse():
@@ -138,12 +140,14 @@ def run_a2a(args):
     print(json.dumps(res), flush=True)
 
 
-def kernel_source_digest(path):
-    """SHA-256 of a source file with its comments and whitespace removed: it
+def kernel_source_digest(paths):
+    """SHA-256 of source files with their comments and whitespace removed: it
     changes when the code does, not when a comment does."""
     import re
-    with open(path) as f:
-        src = f.read()
+    src = ""
+    for path in paths:
+        with open(path) as f:
+            src += f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     src = re.sub(r"//[^\n]*", "", src)
     return hashlib.sha256(re.sub(r"\s+", "", src).encode()).hexdigest()
