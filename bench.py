@@ -228,7 +228,7 @@ def cpu_baseline(inp, seconds, rank=0):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(expert-parallel shares run in sequence on one device); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
