@@ -1,0 +1,31 @@
+"""bench.py's command-line contract on the host: more than one GPU is refused
+with a message and exit status 2 before anything touches a device, and the
+traffic record is looked up by the GEMM source digest."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_traffic_record_follows_the_gemm_source(tmp_path, monkeypatch):
+    import bench
+    src = tmp_path / "k.hip"
+    src.write_text("int f() { return 1; }  // a comment\n")
+    d0 = bench.kernel_source_digest([str(src)])
+    src.write_text("int f() {\n  return 1;  // another comment\n}\n")
+    assert bench.kernel_source_digest([str(src)]) == d0  # comments and spacing only
+    src.write_text("int f() { return 2; }\n")
+    assert bench.kernel_source_digest([str(src)]) != d0  # a code change
+    # a record taken on other source is not used
+    monkeypatch.setattr(bench, "GEMM_SRC", [str(src)])
+    assert bench.gemm_traffic("redundant_slots_zipf") is None
