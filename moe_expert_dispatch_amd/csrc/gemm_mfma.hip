@@ -639,6 +639,8 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
   // (The FP8 down kernel stores directly: the staging addresses do not fit
   // beside its K-loop's registers without spilling.)
   constexpr bool STAGED = OP == 1 && !FP8;
+  // bf16: waves with at most 64 real rows run the two-fragment K-loop
+  constexpr bool HALF_FRAG = true;
   // The next item's slice 0 is requested before this item's epilogue stores,
   // except in the gathered bf16 gate/up kernel, whose SwiGLU epilogue has no
   // registers left for it.
@@ -769,41 +771,51 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
   // waited for and the workgroup synchronises, after which slice d+1 is
   // visible everywhere and buffer d & 1 is no longer read, so the DMA of
   // slice d+2 goes there while block 0 of slice d+1 is read.
-  auto dstep = [&](int d, auto first, auto chk) {
+  // NI (4 or 2) is the number of the wave's 32-row fragments computed: with
+  // at most 64 real rows in the wave's 128, fragments 2 and 3 are padding,
+  // so only MFMAs (j, i < 2) run and only their fragments are read; the DMAs
+  // and the barrier are the same (two DMAs per MFMA in the last block).
+  auto dstep = [&](int d, auto first, auto chk, auto nic) {
+    constexpr int NI = decltype(nic)::value;
+    constexpr int NX = NI == 4 ? 8 : 4;  // MFMAs per K-16 block
+    // MFMA / fragment index of step y: (j, i) = (x >> 2, x & 3)
+    auto xm = [](int y) { return NI == 4 ? y : ((y & 1) | ((y >> 1) << 2)); };
+    auto rd = [](int y) { return NI == 4 ? y < 6 : true; };
     const uint32_t base = smem_base + (uint32_t)(d & 1) * WSTAGE_BYTES;
     const uint32_t nbase = smem_base + (uint32_t)((d + 1) & 1) * WSTAGE_BYTES;
     wait_frags(f0a, f0b);
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      if (x < 6) read8(x, f1a, f1b, base + a_lane[1], base + b_lane[1]);
+    for (int y = 0; y < NX; ++y) {
+      if (rd(y)) read8(xm(y), f1a, f1b, base + a_lane[1], base + b_lane[1]);
       if constexpr (decltype(first)::value)
-        mfma1_first(x, f0a, f0b);
+        mfma1_first(xm(y), f0a, f0b);
       else
-        mfma1(x, f0a, f0b);
+        mfma1(xm(y), f0a, f0b);
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_frags(f1a, f1b);
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      if (x < 6) read8(x, f0a, f0b, base + a_lane[2], base + b_lane[2]);
-      mfma1(x, f1a, f1b);
+    for (int y = 0; y < NX; ++y) {
+      if (rd(y)) read8(xm(y), f0a, f0b, base + a_lane[2], base + b_lane[2]);
+      mfma1(xm(y), f1a, f1b);
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_frags(f0a, f0b);
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      if (x < 6) read8(x, f1a, f1b, base + a_lane[3], base + b_lane[3]);
-      mfma1(x, f0a, f0b);
+    for (int y = 0; y < NX; ++y) {
+      if (rd(y)) read8(xm(y), f1a, f1b, base + a_lane[3], base + b_lane[3]);
+      mfma1(xm(y), f0a, f0b);
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_frags(f1a, f1b);
     vm_wait<0>();
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      dma(cur, x, d + 2, decltype(chk)::value);
-      if (x < 6) read8(x, f0a, f0b, nbase + a_lane[0], nbase + b_lane[0]);
-      mfma1(x, f1a, f1b);
+    for (int y = 0; y < NX; ++y) {
+      dma(cur, (8 / NX) * y, d + 2, decltype(chk)::value);
+      if constexpr (NX == 4) dma(cur, 2 * y + 1, d + 2, decltype(chk)::value);
+      if (rd(y)) read8(xm(y), f0a, f0b, nbase + a_lane[0], nbase + b_lane[0]);
+      mfma1(xm(y), f1a, f1b);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -963,20 +975,34 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
         vm_wait<0>();
         wait_all8();
       } else {
-#pragma unroll
-        for (int x = 0; x < 6; ++x)
-          read8(x, f0a, f0b, smem_base + a_lane[0], smem_base + b_lane[0]);
         const std::true_type checked;
         const std::false_type unchecked;
-        dstep(0, std::true_type{}, checked);
-        // the DMA of slice d + 2 is in range for d < nd - 2
-        int d = 1;
-        for (; d < dlast && d < nd - 2; ++d) dstep(d, std::false_type{}, unchecked);
-        for (; d < dlast; ++d) dstep(d, std::false_type{}, checked);
-        if constexpr (GATHER) {
-          next_setup();
-          dstep(nd - 1, std::false_type{}, checked);
-        }
+        auto kloop = [&](auto nic) {
+          constexpr int NI = decltype(nic)::value;
+          if constexpr (NI == 2) {  // padding rows: defined, never stored
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[j][2] = acc[j][3] = floatx16{};
+            f0a[2] = f0a[3] = f1a[2] = f1a[3] = bf16x8_t{};
+          }
+#pragma unroll
+          for (int x = 0; x < 6; ++x)
+            if (NI == 4 || (x & 3) < 2)
+              read8(x, f0a, f0b, smem_base + a_lane[0], smem_base + b_lane[0]);
+          dstep(0, std::true_type{}, checked, nic);
+          // the DMA of slice d + 2 is in range for d < nd - 2
+          int d = 1;
+          for (; d < dlast && d < nd - 2; ++d) dstep(d, std::false_type{}, unchecked, nic);
+          for (; d < dlast; ++d) dstep(d, std::false_type{}, checked, nic);
+          if constexpr (GATHER) {
+            next_setup();
+            dstep(nd - 1, std::false_type{}, checked, nic);
+          }
+        };
+        // at most 64 real rows in this wave's 128: fragments 2 and 3 are padding
+        if (HALF_FRAG && cur.rows - wm * 128 <= 64)
+          kloop(std::integral_constant<int, 2>{});
+        else
+          kloop(std::integral_constant<int, 4>{});
         vm_wait<0>();
         wait_frags(f0a, f0b);
       }
