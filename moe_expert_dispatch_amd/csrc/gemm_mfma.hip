@@ -377,7 +377,10 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_bf16_kernel(
 //               buffer d & 1) and one LDS read of block 0 of slice d+1.
 // Every slice issues the same 8 DMA instructions per wave (slices past the
 // end use an out-of-range offset and move nothing), so the vmcnt accounting
-// is constant. The next item's first two slices (only slice 0 for the staged
+// is constant. A bf16 wave with at most 64 real rows runs the same schedule
+// with only its first two 32-row fragments (half the MFMAs and reads); a
+// wave with none (the lower half of an item of at most 128 rows) only
+// issues its DMAs and takes the barriers. The next item's first two slices (only slice 0 for the staged
 // bf16 down epilogue, which occupies stage 1) are requested before an item's
 // epilogue stores, so their fetch overlaps the epilogue. The wait for slice 0
 // is then vmcnt(8): the 8 DMAs of slice 1 are younger, and loads complete in
@@ -639,8 +642,6 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
   // (The FP8 down kernel stores directly: the staging addresses do not fit
   // beside its K-loop's registers without spilling.)
   constexpr bool STAGED = OP == 1 && !FP8;
-  // bf16: waves with at most 64 real rows run the two-fragment K-loop
-  constexpr bool HALF_FRAG = true;
   // The next item's slice 0 is requested before this item's epilogue stores,
   // except in the gathered bf16 gate/up kernel, whose SwiGLU epilogue has no
   // registers left for it.
@@ -999,7 +1000,7 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
           }
         };
         // at most 64 real rows in this wave's 128: fragments 2 and 3 are padding
-        if (HALF_FRAG && cur.rows - wm * 128 <= 64)
+        if (cur.rows - wm * 128 <= 64)
           kloop(std::integral_constant<int, 2>{});
         else
           kloop(std::integral_constant<int, 4>{});
