@@ -10,6 +10,7 @@ from .moe_oracle import (  # noqa: F401
     ep_mask_and_remap,
     ep_partition,
     forward,
+    forward_per_pair,
     grouped_down,
     grouped_gate_up,
     permute_indices,

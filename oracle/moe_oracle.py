@@ -142,13 +142,29 @@ def ep_partition(E_global: int, ep_size: int, ep_rank: int) -> Tuple[int, int]:
 
 
 def ep_mask_and_remap(ids, w, start: int, E_local: int):
-    """(local_ids, w_masked, mask) for one rank's expert range [start, start+E_local)."""
+    """(local_ids, w_masked, mask) for one rank's expert range [start, start+E_local).
+
+    [EPMASK] ep_mask_and_remap, stated per pair (t, k) with expert e:
+      - the pair is local when e lies in [start, start + E_local);
+      - its weight is multiplied by 1 when local and by 0 otherwise;
+      - a local pair's local id is e - start; a non-local pair still gets an
+        id inside [0, E_local), the non-negative residue of e modulo E_local,
+        so that non-local pairs spread over the local experts instead of all
+        naming expert 0. (Later stages skip non-local pairs.)
+    """
     ids = _i64(ids)
-    mask = (ids >= start) & (ids < start + E_local)
-    w_masked = _f64(w) * mask.astype(np.float64)
-    local_ids = ids - start
-    non_local = ~mask
-    local_ids[non_local] = np.mod(ids[non_local], E_local)
+    wt = _f64(w)
+    T, K = ids.shape
+    local_ids = np.empty((T, K), dtype=np.int64)
+    w_masked = np.empty((T, K), dtype=np.float64)
+    mask = np.empty((T, K), dtype=bool)
+    for t in range(T):
+        for k in range(K):
+            e = int(ids[t, k])
+            local = start <= e < start + E_local
+            mask[t, k] = local
+            w_masked[t, k] = wt[t, k] * (1.0 if local else 0.0)
+            local_ids[t, k] = e - start if local else e % E_local  # Python %: non-negative
     return local_ids, w_masked, mask
 
 
@@ -360,4 +376,53 @@ def forward(x, logits, w_gate_up, w_down, K: int, renormalize: bool,
         out[m] += (1.0 if routing_on_input else w_masked[m, k, None]) * y[m, k]
     if shared is not None:
         out += _f64(_take_rows(shared, tok))
+    return out
+
+
+# --------------------------------------------------------------------------
+# The same forward pass written literally, one pair at a time: [AUTOTP]
+# Description (each token's routed output is the weighted sum of its selected
+# experts' outputs) with the expert MLP of [A2A] evaluated as three
+# matrix-vector products per pair. It cross-checks forward(), which evaluates
+# each expert's rows together. Pairs are visited expert by expert only so
+# that each expert's weights are decoded to fp64 once; the arithmetic of a
+# pair does not depend on the other pairs.
+# --------------------------------------------------------------------------
+def forward_per_pair(x, logits, w_gate_up, w_down, K: int, renormalize: bool,
+                     ep_size: int = 1, ep_rank: int = 0,
+                     tokens: Optional[Sequence[int]] = None,
+                     topk: Optional[Tuple[np.ndarray, np.ndarray]] = None) -> np.ndarray:
+    """Output rows for `tokens` (default: all), fp64 [n, H]: for each token,
+    the sum over k = 0..K-1 ascending of w_masked[t,k] * MLP_e(x[t]) over its
+    local pairs, MLP_e(v) = Wd[e] (silu(Wg[e] v) * (Wu[e] v))."""
+    T = (logits.shape[0] if topk is None else np.asarray(topk[0]).shape[0])
+    tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    E_global = w_gate_up.shape[0]
+    E_local, start = ep_partition(E_global, ep_size, ep_rank)
+    I = w_down.shape[2]
+    n = tok.size
+    ids = np.empty((n, K), dtype=np.int64)
+    wts = np.empty((n, K))
+    for i, t in enumerate(tok):  # routing of one token at a time
+        if topk is None:
+            ri, rw = route(_f64(logits)[t:t + 1], K, renormalize)
+        else:
+            ri, rw = np.asarray(topk[0])[t:t + 1], _f64(topk[1])[t:t + 1]
+        ids[i], wts[i] = ri[0], rw[0]
+    _, w_masked, mask = ep_mask_and_remap(ids, wts, start, E_local)
+    pairs = {}  # (i, k) -> expert output row
+    for e in sorted({int(ids[i, k]) for i in range(n) for k in range(K) if mask[i, k]}):
+        wgu = _f64(w_gate_up[e])
+        wg, wu, wd = wgu[:I], wgu[I:], _f64(w_down[e])
+        for i in range(n):
+            for k in range(K):
+                if mask[i, k] and ids[i, k] == e:
+                    v = _f64(_take_rows(x, tok[i:i + 1]))[0]
+                    a = silu(wg @ v) * (wu @ v)
+                    pairs[(i, k)] = wd @ a
+    out = np.zeros((n, w_down.shape[1]))
+    for i in range(n):
+        for k in range(K):
+            if mask[i, k]:
+                out[i] += w_masked[i, k] * pairs[(i, k)]
     return out
