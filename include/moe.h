@@ -223,6 +223,11 @@ moe_status_t moe_permute(const void* x, moe_dtype_t dt, int T, int H, int K,
  * device-data precondition (rows beyond max_rows are never touched).
  * H % 8 == 0 and I % 8 == 0. dt MOE_DTYPE_BF16 runs on the matrix cores
  * (MFMA); MOE_DTYPE_F32 uses a vector fused-multiply-add path.
+ * One slot's gate/up panel, 2 * I * H elements, must be under 2^31 bytes
+ * (MOE_ERR_UNSUPPORTED otherwise; the same limit holds for moe_forward and
+ * moe_grouped_gemm_fp8 with their element sizes).
+ * No workspace argument: the tile table of the grouped launch is rebuilt
+ * by every block from `offsets` in its own shared memory.
  */
 moe_status_t moe_grouped_gemm(moe_gemm_op_t op, moe_dtype_t dt, const void* a,
                               const int32_t* offsets, int S, int max_rows, const void* w,
@@ -304,7 +309,17 @@ moe_status_t moe_combine_shared(const void* y, moe_dtype_t y_dt, const int32_t* 
                                 moe_dtype_t shared_dt, void* out, moe_dtype_t out_dt,
                                 int accumulate, hipStream_t stream);
 
-/* Fused forward: one call enqueues every stage in order on one stream. */
+/*
+ * Fused forward: one call enqueues every stage in order on one stream.
+ *   Source: [A2A] walkthrough sequence diagram: one fused MoE op is given the
+ *   tokens, the selected experts and their routing weights (or computes the
+ *   routing itself) and returns the layer's output; its MoE mapping
+ *   configuration carries the EP size and rank and a max-num-tokens field
+ *   that sizes the op's workspace (T_max here). [EPMASK] docstring and
+ *   ep_mask_and_remap (the share's mask and remap); [SLOTS] Description
+ *   (compute over engine-side slots); [AUTOTP] (the weighted sum formed
+ *   before the layer's single reduction, so shares can be summed).
+ */
 typedef struct {
   int T_max;        /* largest T the workspace is sized for ([A2A] max num tokens) */
   int T;            /* tokens in this call, 0 <= T <= T_max */
@@ -324,6 +339,10 @@ typedef struct {
   int routing_on_input; /* apply the routing weights to the expert input (see moe_permute_scaled) */
   float a1_scale;       /* dtype MOE_DTYPE_FP8_E4M3: scale of the quantized expert input */
   float a2_scale;       /* dtype MOE_DTYPE_FP8_E4M3: scale of the quantized SwiGLU output */
+  int gemm_blocks;      /* 0: the grouped GEMMs run one persistent block per compute unit;
+                           n > 0: at most n blocks, leaving the other compute units to work
+                           queued on other streams (for instance a collective running beside
+                           the layer). The output does not depend on it. Negative: error. */
 } moe_config_t;
 
 /* Stage boundaries at which moe_forward records the caller's events. */
@@ -357,6 +376,9 @@ typedef struct {
  * moe_forward_workspace_size -- bytes of device workspace moe_forward needs
  * for cfg->T_max tokens (routing arrays, permutation, permuted rows and the
  * two intermediate activations). Returns 0 for an invalid configuration.
+ *   Source: [A2A] MoE mapping configuration: the workspace is sized by the
+ *   maximum number of tokens, so one allocation serves every call with
+ *   T <= T_max.
  *
  * moe_forward -- route (or take topk_ids / topk_w), slot map, permute,
  * grouped GEMM 1, grouped GEMM 2 and combine, all enqueued on `stream`.

@@ -55,7 +55,8 @@ class _Config(ctypes.Structure):
                 ("renormalize", _i), ("ep_size", _i), ("ep_rank", _i), ("S", _i),
                 ("dtype", _i), ("out_dtype", _i), ("accumulate", _i),
                 ("num_expert_group", _i), ("topk_group", _i), ("routing_on_input", _i),
-                ("a1_scale", ctypes.c_float), ("a2_scale", ctypes.c_float)]
+                ("a1_scale", ctypes.c_float), ("a2_scale", ctypes.c_float),
+                ("gemm_blocks", _i)]
 
 
 class _ForwardArgs(ctypes.Structure):
@@ -365,7 +366,8 @@ class ForwardConfig:
                  S: int, dtype: torch.dtype, out_dtype: Optional[torch.dtype] = None,
                  ep_size: int = 1, ep_rank: int = 0, accumulate: bool = False,
                  T_max: Optional[int] = None, num_expert_group: int = 0, topk_group: int = 0,
-                 routing_on_input: bool = False, a1_scale: float = 1.0, a2_scale: float = 1.0):
+                 routing_on_input: bool = False, a1_scale: float = 1.0, a2_scale: float = 1.0,
+                 gemm_blocks: int = 0):
         self.T, self.H, self.I, self.E_global, self.K = T, H, I, E_global, K
         self.renormalize, self.S, self.dtype = bool(renormalize), S, dtype
         # FP8 (dtype FP8): x, shared_out and the default out are bf16
@@ -375,13 +377,14 @@ class ForwardConfig:
         self.T_max = T if T_max is None else T_max
         self.num_expert_group, self.topk_group = num_expert_group, topk_group
         self.routing_on_input = bool(routing_on_input)
+        self.gemm_blocks = int(gemm_blocks)  # 0: one persistent GEMM block per compute unit
 
     def c_struct(self) -> _Config:
         return _Config(self.T_max, self.T, self.H, self.I, self.E_global, self.K,
                        int(self.renormalize), self.ep_size, self.ep_rank, self.S,
                        _DT[self.dtype], _DT[self.out_dtype], int(self.accumulate),
                        self.num_expert_group, self.topk_group, int(self.routing_on_input),
-                       self.a1_scale, self.a2_scale)
+                       self.a1_scale, self.a2_scale, self.gemm_blocks)
 
 
 def forward_workspace_size(cfg: ForwardConfig) -> int:

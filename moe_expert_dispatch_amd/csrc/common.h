@@ -172,8 +172,17 @@ inline moe_status_t launch_status() {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-// Number of compute units of the current device (queried once per device).
+// Number of compute units of the current device (queried on every call).
 int device_cu_count();
+
+// A slot's weight panel (the 2I x H gate/up rows, the larger of the two
+// matrices) must stay below 2^31 bytes: the GEMMs address it through a
+// buffer resource with 32-bit offsets and use 2^31 as their out-of-range
+// offset.
+inline bool weight_panel_ok(int H, int I, int elem_bytes) {
+  return 2ull * (unsigned long long)H * (unsigned long long)I * (unsigned)elem_bytes <
+         (1ull << 31);
+}
 
 // ---------------------------------------------------------------- FP8
 // Quantization to OCP E4M3 with one scale per tensor: code = E4M3 value
@@ -288,9 +297,11 @@ moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
                             hipStream_t stream, int seg_cap = 0,
                             const float* pair_w = nullptr, const FusedQuant* quant = nullptr);
 
+// max_blocks > 0 caps the persistent GEMM grid (default: one block per
+// compute unit); the results do not depend on the grid.
 moe_status_t launch_gemm_bf16(moe_gemm_op_t op, const void* a, const int32_t* offsets, int S,
                               int max_rows, const void* w, int H, int I, void* c,
-                              hipStream_t stream);
+                              hipStream_t stream, int max_blocks = 0);
 // Gate/up product with the permutation's gather folded into the operand fetch:
 // row r of the permuted order is token sorted_pairs[r] / K of x [T, H]. Only
 // for shapes where gemm_bf16_gather_ok(T, H) holds.
@@ -299,7 +310,7 @@ moe_status_t launch_gemm_bf16_gate_up_gathered(const void* x, int T, int K,
                                                const int32_t* sorted_pairs,
                                                const int32_t* offsets, int S, int max_rows,
                                                const void* w, int H, int I, void* c,
-                                               hipStream_t stream);
+                                               hipStream_t stream, int max_blocks = 0);
 moe_status_t launch_gemm_f32(moe_gemm_op_t op, const void* a, const int32_t* offsets, int S,
                              int max_rows, const void* w, int H, int I, void* c,
                              hipStream_t stream);
@@ -313,13 +324,14 @@ bool gemm_fp8_gather_ok(int T, int H);
 moe_status_t launch_gemm_fp8(moe_gemm_op_t op, const uint8_t* a, float a_scale,
                              const int32_t* offsets, int S, int max_rows, const uint8_t* w,
                              const float* w_scale, int H, int I, void* c, float out_scale,
-                             hipStream_t stream);
+                             hipStream_t stream, int max_blocks = 0);
 moe_status_t launch_gemm_fp8_gate_up_gathered(const uint8_t* xq, int T, int K,
                                               const int32_t* sorted_pairs,
                                               const int32_t* offsets, int S, int max_rows,
                                               const uint8_t* w, const float* w_scale,
                                               float a_scale, int H, int I, void* c,
-                                              float out_scale, hipStream_t stream);
+                                              float out_scale, hipStream_t stream,
+                                              int max_blocks = 0);
 // q[i] = E4M3 code of clamp(x[i] * (1 / scale), -448, 448), rounded to nearest even.
 moe_status_t launch_quantize_fp8(const void* x, bool x_bf16, int64_t n, float scale, uint8_t* q,
                                  hipStream_t stream);

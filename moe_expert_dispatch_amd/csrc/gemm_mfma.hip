@@ -1043,13 +1043,14 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
 
 namespace {
 
-int gemm_grid(int max_rows, int S, int N, int BN) {
+int gemm_grid(int max_rows, int S, int N, int BN, int max_blocks) {
   // Upper bound on items: sum_s ceil(n_s/BM) <= ceil(max_rows/BM) + min(S, max_rows),
   // plus the holes of partial item groups.
   const long long max_items =
       (long long)(ceil_div(max_rows, BM) + (S < max_rows ? S : max_rows) + XCD_ITEMS) *
       (ceil_div(N, BN) + 8);
-  const int G = device_cu_count();
+  int G = device_cu_count();
+  if (max_blocks > 0 && max_blocks < G) G = max_blocks;
   return max_items < G ? (int)max_items : G;
 }
 
@@ -1060,12 +1061,12 @@ bool dma_ok(int Kd) { return Kd % WBK == 0 && Kd >= 2 * WBK; }
 
 moe_status_t launch_gemm_bf16(moe_gemm_op_t op, const void* a, const int32_t* offsets, int S,
                               int max_rows, const void* w, int H, int I, void* c,
-                              hipStream_t stream) {
+                              hipStream_t stream, int max_blocks) {
   if (max_rows == 0) return MOE_OK;
   const int N = (op == MOE_GEMM_GATE_UP_SWIGLU) ? I : H;
   const int Kd = (op == MOE_GEMM_GATE_UP_SWIGLU) ? H : I;
   const int BN = (op == MOE_GEMM_GATE_UP_SWIGLU) ? BROWS / 2 : BROWS;
-  const int G = gemm_grid(max_rows, S, N, BN);
+  const int G = gemm_grid(max_rows, S, N, BN, max_blocks);
   const uint4* a4 = static_cast<const uint4*>(a);
   const uint4* w4 = static_cast<const uint4*>(w);
   uint16_t* c16 = static_cast<uint16_t*>(c);
@@ -1095,10 +1096,10 @@ moe_status_t launch_gemm_bf16_gate_up_gathered(const void* x, int T, int K,
                                                const int32_t* sorted_pairs,
                                                const int32_t* offsets, int S, int max_rows,
                                                const void* w, int H, int I, void* c,
-                                               hipStream_t stream) {
+                                               hipStream_t stream, int max_blocks) {
   if (!gemm_bf16_gather_ok(T, H)) return MOE_ERR_UNSUPPORTED;
   if (max_rows == 0) return MOE_OK;
-  const int G = gemm_grid(max_rows, S, I, BROWS / 2);
+  const int G = gemm_grid(max_rows, S, I, BROWS / 2, max_blocks);
   grouped_gemm_dma_kernel<0, true, false><<<G, NTHR8, 0, stream>>>(
       static_cast<const uint4*>(x), offsets, S, static_cast<const uint4*>(w), I, H, c,
       sorted_pairs, K, T, 1.0f, nullptr, 1.0f);
@@ -1115,13 +1116,13 @@ bool gemm_fp8_gather_ok(int T, int H) {
 moe_status_t launch_gemm_fp8(moe_gemm_op_t op, const uint8_t* a, float a_scale,
                              const int32_t* offsets, int S, int max_rows, const uint8_t* w,
                              const float* w_scale, int H, int I, void* c, float out_scale,
-                             hipStream_t stream) {
+                             hipStream_t stream, int max_blocks) {
   const bool gu = op == MOE_GEMM_GATE_UP_SWIGLU;
   const int N = gu ? I : H;
   const int Kd = gu ? H : I;
   if (!gemm_fp8_ok(Kd)) return MOE_ERR_UNSUPPORTED;
   if (max_rows == 0) return MOE_OK;
-  const int G = gemm_grid(max_rows, S, N, gu ? BROWS / 2 : BROWS);
+  const int G = gemm_grid(max_rows, S, N, gu ? BROWS / 2 : BROWS, max_blocks);
   const uint4* a4 = reinterpret_cast<const uint4*>(a);
   const uint4* w4 = reinterpret_cast<const uint4*>(w);
   if (gu)
@@ -1138,10 +1139,11 @@ moe_status_t launch_gemm_fp8_gate_up_gathered(const uint8_t* xq, int T, int K,
                                               const int32_t* offsets, int S, int max_rows,
                                               const uint8_t* w, const float* w_scale,
                                               float a_scale, int H, int I, void* c,
-                                              float out_scale, hipStream_t stream) {
+                                              float out_scale, hipStream_t stream,
+                                              int max_blocks) {
   if (!gemm_fp8_gather_ok(T, H)) return MOE_ERR_UNSUPPORTED;
   if (max_rows == 0) return MOE_OK;
-  const int G = gemm_grid(max_rows, S, I, BROWS / 2);
+  const int G = gemm_grid(max_rows, S, I, BROWS / 2, max_blocks);
   grouped_gemm_dma_kernel<0, true, true><<<G, NTHR8, 0, stream>>>(
       reinterpret_cast<const uint4*>(xq), offsets, S, reinterpret_cast<const uint4*>(w), I, H,
       c, sorted_pairs, K, T, a_scale, w_scale, 1.0f / out_scale);

@@ -6,25 +6,18 @@
 // selected experts and routing weights; MoE mapping configuration with EP
 // size / rank and max num tokens sizing the workspace); vLLM
 // ep_fused_moe_patch.py _ep_init (E % ep_size asserted, start = rank * E_l).
-#include <atomic>
-
 #include "common.h"
 
 namespace moe {
 
+// Asked of the runtime on every GEMM launch (a host-side attribute read), so
+// the library keeps no per-device state for it.
 int device_cu_count() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 1;
-  if (dev >= 0 && dev < 64) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       n <= 0)
-    n = 1;
-  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return 1;
   return n;
 }
 
@@ -86,12 +79,16 @@ moe_status_t check_permute(const void* x, moe_dtype_t dt, int T, int H, int K,
   return MOE_OK;
 }
 
+// elem_bytes: operand bytes for the weight-panel limit (0: those of dt).
 moe_status_t check_gemm(moe_gemm_op_t op, moe_dtype_t dt, const void* a, const int32_t* offsets,
-                        int S, int max_rows, const void* w, int H, int I, const void* c) {
+                        int S, int max_rows, const void* w, int H, int I, const void* c,
+                        int elem_bytes = 0) {
   if (op != MOE_GEMM_GATE_UP_SWIGLU && op != MOE_GEMM_DOWN) return MOE_ERR_INVALID_ARG;
   if (S < 1 || max_rows < 0 || H < 1 || I < 1) return MOE_ERR_INVALID_ARG;
   if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
   if (S > MOE_MAX_SLOTS || H % 8 != 0 || I % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!weight_panel_ok(H, I, elem_bytes > 0 ? elem_bytes : dtype_bytes(dt)))
+    return MOE_ERR_UNSUPPORTED;
   if ((long long)max_rows * (H > I ? H : I) >= (1LL << 40)) return MOE_ERR_UNSUPPORTED;
   if (!offsets) return MOE_ERR_INVALID_ARG;
   if (max_rows > 0 && (!a || !w || !c)) return MOE_ERR_INVALID_ARG;
@@ -115,9 +112,10 @@ moe_status_t check_combine(const void* y, moe_dtype_t y_dt, const int32_t* pair_
 
 moe_status_t launch_gemm(moe_gemm_op_t op, moe_dtype_t dt, const void* a, const int32_t* offsets,
                          int S, int max_rows, const void* w, int H, int I, void* c,
-                         hipStream_t stream) {
-  return dt == MOE_DTYPE_BF16 ? launch_gemm_bf16(op, a, offsets, S, max_rows, w, H, I, c, stream)
-                              : launch_gemm_f32(op, a, offsets, S, max_rows, w, H, I, c, stream);
+                         hipStream_t stream, int max_blocks = 0) {
+  return dt == MOE_DTYPE_BF16
+             ? launch_gemm_bf16(op, a, offsets, S, max_rows, w, H, I, c, stream, max_blocks)
+             : launch_gemm_f32(op, a, offsets, S, max_rows, w, H, I, c, stream);
 }
 
 // Workspace of moe_forward, carved in this order (each 256-byte aligned).
@@ -201,6 +199,8 @@ moe_status_t check_config(const moe_config_t* c) {
   if (c->E_global > MOE_MAX_EXPERTS || c->K > MOE_MAX_TOPK || c->S > MOE_MAX_SLOTS)
     return MOE_ERR_UNSUPPORTED;
   if (c->H % 8 != 0 || c->I % 8 != 0 || !pairs_fit(c->T_max, c->K)) return MOE_ERR_UNSUPPORTED;
+  if (!weight_panel_ok(c->H, c->I, dtype_bytes(c->dtype))) return MOE_ERR_UNSUPPORTED;
+  if (c->gemm_blocks < 0) return MOE_ERR_INVALID_ARG;
   const long long P = (long long)c->T_max * c->K;
   if (P * (c->H > c->I ? c->H : c->I) >= (1LL << 40)) return MOE_ERR_UNSUPPORTED;
   if (c->num_expert_group != 0 || c->topk_group != 0) {
@@ -359,6 +359,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_forward_args_t* args
   uint8_t* xq = reinterpret_cast<uint8_t*>(base + L.xq);
   void* y = x_perm;  // grouped GEMM 1 has consumed x_perm when GEMM 2 writes
   const bool fp8 = cfg->dtype == MOE_DTYPE_FP8_E4M3;
+  const int gb = cfg->gemm_blocks;  // persistent GEMM grid cap (0: one block per CU)
 
   auto mark = [&](int ev) -> moe_status_t {
     if (args->events[ev] && hipEventRecord(args->events[ev], stream) != hipSuccess)
@@ -402,21 +403,21 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_forward_args_t* args
   if (fp8)
     MOE_TRY(launch_gemm_fp8_gate_up_gathered(
         xq, T, K, sorted_pairs, offsets, S, T * K, static_cast<const uint8_t*>(args->w_gate_up),
-        args->w_gate_up_scale, cfg->a1_scale, H, I, act, cfg->a2_scale, stream));
+        args->w_gate_up_scale, cfg->a1_scale, H, I, act, cfg->a2_scale, stream, gb));
   else if (fused_gather)
     MOE_TRY(launch_gemm_bf16_gate_up_gathered(args->x, T, K, sorted_pairs, offsets, S, T * K,
-                                              args->w_gate_up, H, I, act, stream));
+                                              args->w_gate_up, H, I, act, stream, gb));
   else
     MOE_TRY(launch_gemm(MOE_GEMM_GATE_UP_SWIGLU, cfg->dtype, x_perm, offsets, S, T * K,
-                        args->w_gate_up, H, I, act, stream));
+                        args->w_gate_up, H, I, act, stream, gb));
   MOE_TRY(mark(MOE_EV_GATE_UP));
   if (fp8)
     MOE_TRY(launch_gemm_fp8(MOE_GEMM_DOWN, static_cast<const uint8_t*>(act), cfg->a2_scale,
                             offsets, S, T * K, static_cast<const uint8_t*>(args->w_down),
-                            args->w_down_scale, H, I, y, 1.0f, stream));
+                            args->w_down_scale, H, I, y, 1.0f, stream, gb));
   else
     MOE_TRY(launch_gemm(MOE_GEMM_DOWN, cfg->dtype, act, offsets, S, T * K, args->w_down, H, I,
-                        y, stream));
+                        y, stream, gb));
   MOE_TRY(mark(MOE_EV_DOWN));
   const moe_dtype_t ydt = fp8 ? MOE_DTYPE_BF16 : cfg->dtype;
   MOE_TRY(launch_combine(y, ydt, pair_row, on_input ? nullptr : w_masked, T, K, H, args->out,
@@ -439,8 +440,10 @@ moe_status_t moe_grouped_gemm_fp8(moe_gemm_op_t op, const uint8_t* a, float a_sc
                                   const int32_t* offsets, int S, int max_rows, const uint8_t* w,
                                   const float* w_scale, int H, int I, void* c, float c_scale,
                                   hipStream_t stream) {
-  // the shape, pointer and alignment rules of moe_grouped_gemm
-  const moe_status_t st = check_gemm(op, MOE_DTYPE_BF16, a, offsets, S, max_rows, w, H, I, c);
+  // the shape, pointer and alignment rules of moe_grouped_gemm, with the
+  // weight-panel limit taken for one-byte codes
+  const moe_status_t st =
+      check_gemm(op, MOE_DTYPE_BF16, a, offsets, S, max_rows, w, H, I, c, 1);
   if (st != MOE_OK) return st;
   if (!scale_ok(a_scale) || (op == MOE_GEMM_GATE_UP_SWIGLU && !scale_ok(c_scale)))
     return MOE_ERR_INVALID_ARG;

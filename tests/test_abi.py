@@ -264,3 +264,31 @@ def test_forward_fp8_config_validation(so):
     st = so.moe_forward(ctypes.byref(ok.c_struct()), ctypes.byref(args), ctypes.c_void_p(256),
                         n, None)
     assert st == INVALID
+
+
+def test_weight_panel_limit(so):
+    """A slot's gate/up panel (2 * I * H elements) must stay under 2^31 bytes:
+    the GEMMs address it with 32-bit buffer offsets and use 2^31 as their
+    out-of-range offset. Zero rows: validation runs, nothing is launched."""
+    fake = ctypes.c_void_p(256)
+    g = so.moe_grouped_gemm
+    for op in (0, 1):
+        assert g(op, 1, fake, fake, 4, 0, fake, 16384, 32768, fake, None) == UNSUPPORTED
+        assert g(op, 1, fake, fake, 4, 0, fake, 16384, 32760, fake, None) == 0
+        assert g(op, 0, fake, fake, 4, 0, fake, 16384, 16384, fake, None) == UNSUPPORTED  # f32
+        assert g(op, 0, fake, fake, 4, 0, fake, 16384, 16376, fake, None) == 0
+    f8 = so.moe_grouped_gemm_fp8
+    for op in (0, 1):
+        assert f8(op, fake, 1.0, fake, 4, 0, fake, fake, 32768, 32768, fake, 1.0,
+                  None) == UNSUPPORTED
+        assert f8(op, fake, 1.0, fake, 4, 0, fake, fake, 32768, 32640, fake, 1.0, None) == 0
+    ws = so.moe_forward_workspace_size
+    assert ws(ctypes.byref(_cfg(H=16384, I=32768).c_struct())) == 0
+    assert ws(ctypes.byref(_cfg(H=16384, I=32760, T=1).c_struct())) > 0
+
+
+def test_gemm_blocks_validation(so):
+    ws = so.moe_forward_workspace_size
+    assert ws(ctypes.byref(_cfg(gemm_blocks=-1).c_struct())) == 0
+    assert ws(ctypes.byref(_cfg(gemm_blocks=8).c_struct())) == \
+        ws(ctypes.byref(_cfg().c_struct()))

@@ -7,9 +7,14 @@ workload shape, plus the invariants the pages fix:
     replica serves a token (TensorRT-LLM PR #4495, Description);
   - the expert-parallel partial outputs sum to the full output (vLLM
     ep_reduce_output; DeepSpeed PR #6964 single reduction per layer).
-Full-size workloads compare sampled tokens (the oracle computes them one by
-one) and check every index array bit for bit through the staged entry points;
-medium shapes spanning several tiles with ragged tails compare every output.
+Full-size workloads compare the tokens of a covering sample -- at least one
+sampled row in every 128-row piece of every slot, so every GEMM work item and
+every ragged tail is checked against the oracle -- and check every index
+array bit for bit through the staged entry points. Medium shapes spanning
+several tiles with ragged tails compare every output, also with the GEMM grid
+capped at a few blocks so that each block loops over many work items, and a
+16384-token shape whose launches give every block several items compares
+every output at the full grid.
 """
 import numpy as np
 import pytest
@@ -17,7 +22,8 @@ import torch
 
 import moe_expert_dispatch_amd as moe
 import oracle
-from gpu_common import BF16_TOL, F32_TOL, announce, assert_close, device, np64, rel_fro
+from gpu_common import (BF16_TOL, F32_TOL, announce, assert_close, covering_tokens, device,
+                        np64, rel_fro)
 from workloads import (CONFIGS, WorkloadConfig, build_slot_table, identity_slot_table,
                        make_inputs, slot_weights)
 
@@ -89,6 +95,22 @@ def sample_tokens(T, n, seed=0):
     return np.sort(np.concatenate([[0, T - 1], mid]))
 
 
+def oracle_covering(inp, ep_rank=0, replicas=False, seed=0):
+    """Covering sample of one share's permutation, as the oracle computes it
+    (routing, EP mask, slot table, counting sort)."""
+    cfg = inp.cfg
+    ids, w = oracle_route(inp)
+    if replicas:
+        ro, rs, se = build_slot_table(cfg.E_local, inp.replicated_experts())
+        ro, rs, S = ro.numpy(), rs.numpy(), int(se.numel())
+    else:
+        ro = rs = None
+        S = cfg.E_local
+    slot, _, mask = oracle.slot_map(ids, w, cfg.E, cfg.ep_size, ep_rank, ro, rs)
+    off, sp, pr = oracle.permute_indices(slot, mask, S)
+    return covering_tokens(off, sp, pr, cfg.K, seed=seed)
+
+
 def check_staged_indices(inp, dev, ep_rank=0, replicas=False):
     """Route, slot map and permutation of the full workload, bit for bit."""
     cfg = inp.cfg
@@ -153,15 +175,15 @@ def test_forward_tiny_fp32_all_tokens(dev):
     check_staged_indices(inp, dev)
 
 
-@pytest.mark.parametrize("name,n_sample", [("qwen2_moe_bf16", 64), ("deepseek_v2_bf16", 24),
-                                           ("deepseek_v2_grouped_bf16", 24)])
-def test_forward_full_size_sampled(dev, name, n_sample):
+@pytest.mark.parametrize("name", ["qwen2_moe_bf16", "deepseek_v2_bf16",
+                                  "deepseek_v2_grouped_bf16"])
+def test_forward_full_size_covering(dev, name):
     inp = inputs(name)
-    cfg = inp.cfg
-    announce(f"forward {name} full size, {n_sample} sampled tokens")
+    tokens = oracle_covering(inp)
+    announce(f"forward {name} full size, {tokens.size} covering tokens")
     out = run_forward(inp, dev)
     torch.cuda.synchronize()
-    compare_tokens(out, inp, sample_tokens(cfg.T, n_sample), what=name)
+    compare_tokens(out, inp, tokens, what=name)
     announce(f"staged indices {name}")
     check_staged_indices(inp, dev)
 
@@ -172,10 +194,11 @@ def test_forward_ep_shares_sum_to_full(dev):
     tokens = sample_tokens(cfg.T, 32, seed=2)
     acc = torch.zeros(cfg.T, cfg.H, dtype=torch.float32, device=dev)
     for r in range(cfg.ep_size):
-        announce(f"forward ep share rank {r}")
+        cover = oracle_covering(inp, ep_rank=r, seed=r)
+        announce(f"forward ep share rank {r}, {cover.size} covering tokens")
         share = run_forward(inp, dev, ep_rank=r)
         torch.cuda.synchronize()
-        compare_tokens(share, inp, tokens, ep_rank=r, what=f"share {r}")
+        compare_tokens(share, inp, cover, ep_rank=r, what=f"share {r}")
         run_forward(inp, dev, ep_rank=r, out=acc, accumulate=True, out_dtype=torch.float32)
         if r == 1:
             check_staged_indices(inp, dev, ep_rank=1)
@@ -186,7 +209,7 @@ def test_forward_ep_shares_sum_to_full(dev):
     torch.cuda.synchronize()
     assert_close(np64(acc.cpu()), np64(full.cpu()), BF16_TOL, "sum of shares vs full")
     assert rel_fro(np64(acc.cpu()), np64(full.cpu())) < 1e-2
-    compare_tokens(full, full_inp, tokens, what="full layer")
+    compare_tokens(full, full_inp, oracle_covering(full_inp, seed=9), what="full layer")
     # oracle identity on the sampled tokens
     parts = sum(oracle.forward(inp.x, inp.logits, inp.w_gate_up, inp.w_down, cfg.K,
                                cfg.renormalize, cfg.ep_size, r, tokens=tokens)
@@ -198,9 +221,8 @@ def test_forward_ep_shares_sum_to_full(dev):
 
 def test_forward_replicated_slots(dev):
     inp = inputs("redundant_slots_zipf")
-    cfg = inp.cfg
-    tokens = sample_tokens(cfg.T, 48, seed=3)
-    announce("forward zipf 80 slots (replicas)")
+    tokens = oracle_covering(inp, replicas=True, seed=3)
+    announce(f"forward zipf 80 slots (replicas), {tokens.size} covering tokens")
     rep = run_forward(inp, dev, replicas=True)
     torch.cuda.synchronize()
     compare_tokens(rep, inp, tokens, what="replicas")
@@ -392,3 +414,104 @@ def test_forward_grouped_routing(dev):
     # the grouping must matter for this input, or the test proves nothing
     plain, _ = oracle.route(inp.logits.numpy(), cfg.K, True)
     assert not np.array_equal(plain, ids)
+
+
+# ------------------------------------------------------------------ full size, options
+@pytest.mark.parametrize("name", ["qwen2_moe_shared_bf16", "qwen2_moe_input_routing_bf16"])
+def test_forward_full_size_options_covering(dev, name):
+    """The 60-expert layer with a shared-expert output added in the combine,
+    and with the routing weights applied on the expert input (the scaled rows
+    are gathered by the permutation, not folded into the gate/up GEMM)."""
+    inp = inputs(name)
+    cfg = inp.cfg
+    tokens = oracle_covering(inp)
+    announce(f"forward {name} full size, {tokens.size} covering tokens")
+    shared = None
+    if cfg.shared_expert:
+        shared = torch.randn(cfg.T, cfg.H, generator=torch.Generator().manual_seed(1)).to(
+            torch.bfloat16)
+    fc = moe.ForwardConfig(T=cfg.T, H=cfg.H, I=cfg.I, E_global=cfg.E, K=cfg.K,
+                           renormalize=cfg.renormalize, S=cfg.E, dtype=torch.bfloat16,
+                           routing_on_input=cfg.routing_on_input)
+    out = moe.forward(fc, inp.x.to(dev), inp.w_gate_up.to(dev), inp.w_down.to(dev),
+                      logits=inp.logits.to(dev),
+                      shared_out=None if shared is None else shared.to(dev))
+    torch.cuda.synchronize()
+    got = np64(out[torch.from_numpy(tokens).to(dev)].cpu())
+    ref = oracle.forward(inp.x, inp.logits, inp.w_gate_up, inp.w_down, cfg.K, cfg.renormalize,
+                         tokens=tokens, routing_on_input=cfg.routing_on_input, shared=shared)
+    assert_close(got, ref, BF16_TOL, name)
+
+
+# ------------------------------------------------------------------ many items per block
+MULTI_ITEM = WorkloadConfig("mi", T=16384, H=512, I=512, E=8, K=4, renormalize=True,
+                            dtype="bf16", router="gauss_bias", bias_std=0.3, seed=51)
+
+
+def test_forward_many_items_per_block_all_tokens(dev):
+    """16384 tokens, H = I = 512, 8 experts, top-4: the gate/up launch has
+    about 1050 work items and the down launch about 525, so on a full grid
+    every block computes several items in a row (the next item's first
+    K-slices fetched during the previous epilogue, the gathered token rows
+    set up before the last slice). Every output is compared with the oracle,
+    and the run with the grid capped at 16 blocks is bit-identical."""
+    inp = make_inputs(MULTI_ITEM)
+    cfg = inp.cfg
+    ids, w = oracle.route(inp.logits, cfg.K, cfg.renormalize)
+    counts = np.bincount(ids.ravel(), minlength=cfg.E)
+    announce(f"forward many items per block, slot rows {counts.tolist()}")
+    out = run_forward(inp, dev)
+    fc = moe.ForwardConfig(T=cfg.T, H=cfg.H, I=cfg.I, E_global=cfg.E, K=cfg.K,
+                           renormalize=cfg.renormalize, S=cfg.E, dtype=torch.bfloat16,
+                           gemm_blocks=16)
+    capped = moe.forward(fc, inp.x.to(dev), inp.w_gate_up.to(dev), inp.w_down.to(dev),
+                         logits=inp.logits.to(dev))
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp.x, inp.logits, inp.w_gate_up, inp.w_down, cfg.K, cfg.renormalize)
+    assert_close(np64(out.cpu()), ref, BF16_TOL, "many items per block")
+    assert rel_fro(np64(out.cpu()), ref) < 1e-2
+    assert torch.equal(out.view(torch.int16), capped.view(torch.int16))
+
+
+@pytest.mark.parametrize("name,blocks", [("bf16_ragged", 3), ("bf16_odd_dims", 2),
+                                         ("bf16_ep_rank1", 5), ("bf16_replicas", 4),
+                                         ("bf16_k_eq_e", 1), ("bf16_big_tiles", 8)])
+def test_forward_medium_capped_grid(dev, name, blocks):
+    """The medium shapes with the persistent GEMM grid capped at a few blocks:
+    each block then runs many items in a row, mixing full, half-empty and
+    two-fragment items and items of different slots. Every output against
+    the oracle, and bit-identical to the full-grid run."""
+    cfg = MEDIUM[name]
+    inp = make_inputs(cfg)
+    ep_rank = cfg.ep_size - 1
+    announce(f"forward medium {name}, GEMM grid capped at {blocks} blocks")
+    shares = share_tensors(inp, dev, ep_rank, replicas=cfg.n_replicated > 0)
+    full = run_forward(inp, dev, ep_rank=ep_rank, shares=shares)
+    wgu, wd, ro, rs, S = shares
+    fc = moe.ForwardConfig(T=cfg.T, H=cfg.H, I=cfg.I, E_global=cfg.E, K=cfg.K,
+                           renormalize=cfg.renormalize, S=S, dtype=_TDT[cfg.dtype],
+                           ep_size=cfg.ep_size, ep_rank=ep_rank, gemm_blocks=blocks)
+    capped = moe.forward(fc, inp.x.to(dev), wgu, wd, logits=inp.logits.to(dev), rep_off=ro,
+                         rep_slots=rs)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp.x, inp.logits, inp.w_gate_up, inp.w_down, cfg.K, cfg.renormalize,
+                         cfg.ep_size, ep_rank)
+    assert_close(np64(capped.cpu()), ref, tol_of(cfg), name)
+    assert torch.equal(full.view(torch.int16), capped.view(torch.int16))
+
+
+def test_forward_input_routing_capped_grid(dev):
+    """Input-side routing runs the gate/up GEMM on the permuted rows (not the
+    gathered kernel): with the grid capped, every output against the oracle."""
+    cfg = MEDIUM["bf16_big_tiles"]
+    inp = make_inputs(cfg)
+    announce("forward input-side routing, GEMM grid capped at 4 blocks")
+    fc = moe.ForwardConfig(T=cfg.T, H=cfg.H, I=cfg.I, E_global=cfg.E, K=cfg.K,
+                           renormalize=cfg.renormalize, S=cfg.E, dtype=torch.bfloat16,
+                           routing_on_input=True, gemm_blocks=4)
+    got = moe.forward(fc, inp.x.to(dev), inp.w_gate_up.to(dev), inp.w_down.to(dev),
+                      logits=inp.logits.to(dev))
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp.x, inp.logits, inp.w_gate_up, inp.w_down, cfg.K, cfg.renormalize,
+                         routing_on_input=True)
+    assert_close(np64(got.cpu()), ref, BF16_TOL, "input routing, capped grid")

@@ -247,9 +247,19 @@ def _gemm_case(dev, counts, H, I, dtype, seed, sample=None):
             assert rel_fro(np64(c1h[:rows]), ref1) < 5e-3
             assert rel_fro(np64(c2h[:rows]), ref2) < 5e-3
     else:
-        # sampled rows: regroup them by slot with their own offsets
+        # sampled rows: one random row in every 128-row piece of every slot
+        # (every work item and both halves of its row tile) plus each slot's
+        # last row; regrouped by slot with their own offsets
         rng = np.random.default_rng(seed)
-        rsel = np.sort(rng.choice(rows, size=min(sample, rows), replace=False))
+        o = off.numpy()
+        pick = []
+        for s_ in range(S):
+            lo_s, hi_s = int(o[s_]), int(o[s_ + 1])
+            for lo in range(lo_s, hi_s, sample):
+                pick.append(int(rng.integers(lo, min(lo + sample, hi_s))))
+            if hi_s > lo_s:
+                pick.append(hi_s - 1)
+        rsel = np.unique(np.asarray(pick, dtype=np.int64))
         slot_of = np.searchsorted(off.numpy(), rsel, side="right") - 1
         sub_off = _offsets(np.bincount(slot_of, minlength=S))
         ref1 = oracle.grouped_gate_up(x[rsel], sub_off, wgu, I)
@@ -265,6 +275,10 @@ GEMM_CASES = {
     "many_small": ([3, 0, 0, 1, 2, 0, 9, 4] * 8, 128, 64, torch.bfloat16),
     "wide_n": ([257, 31], 512, 384, torch.bfloat16),
     "all_empty": ([0, 0, 0], 64, 64, torch.bfloat16),
+    # about 1050 gate/up and 525 down items: several per block on the full
+    # grid; last tiles of 37, 100, 128, 129, 200, 255, 64 and 65 rows
+    "many_items": ([8229, 0, 8292, 8320, 8321, 8392, 8191, 8256, 8257], 512, 512,
+                   torch.bfloat16),
     "f32": ([5, 0, 40, 17, 66], 128, 256, torch.float32),
 }
 
@@ -278,7 +292,8 @@ def test_grouped_gemm_parity(dev, name):
 
 def test_grouped_gemm_zipf_full_size(dev):
     """Row counts of the redundant-slot workload at its full shape (H=4096,
-    I=1024, 131072 rows over 80 slots); sampled rows against the oracle."""
+    I=1024, 131072 rows over 80 slots); a row in every 128-row piece of every
+    slot, and each slot's last row, against the oracle."""
     cfg = CONFIGS["redundant_slots_zipf"]
     inp = make_inputs(cfg, with_weights=False)
     ro, rs, _ = build_slot_table(cfg.E_local, inp.replicated_experts())
@@ -286,7 +301,7 @@ def test_grouped_gemm_zipf_full_size(dev):
     slot, _, mask = oracle.slot_map(ids, w, cfg.E, 1, 0, ro.numpy(), rs.numpy())
     counts = np.bincount(slot[mask == 1], minlength=cfg.S)
     announce(f"grouped_gemm zipf full size counts max={counts.max()} min={counts.min()}")
-    _gemm_case(dev, counts.tolist(), cfg.H, cfg.I, torch.bfloat16, seed=3, sample=96)
+    _gemm_case(dev, counts.tolist(), cfg.H, cfg.I, torch.bfloat16, seed=3, sample=128)
 
 
 # ------------------------------------------------------------------ combine
