@@ -37,8 +37,8 @@ from .moe_oracle import _f64, _i64, _take_rows, ep_mask_and_remap, ep_partition,
 E4M3_MAX = 448.0
 
 
-def e4m3_decode(codes) -> np.ndarray:
-    """fp64 values of E4M3 codes (uint8 array-like), by the bit-field definition."""
+def _decode_fields(codes) -> np.ndarray:
+    """fp64 values of E4M3 codes by the bit-field definition."""
     c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
     s = c >> 7
     e = (c >> 3) & 15
@@ -46,6 +46,16 @@ def e4m3_decode(codes) -> np.ndarray:
     mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
     val = np.where(s == 1, -mag, mag)
     return np.where((e == 15) & (m == 7), np.nan, val)
+
+
+# the definition evaluated once for each of the 256 codes
+_DECODED = _decode_fields(np.arange(256))
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """fp64 values of E4M3 codes (uint8 array-like): the bit-field definition,
+    looked up per code (large weight tensors decode in one indexing pass)."""
+    return _DECODED[np.asarray(codes, dtype=np.uint8)]
 
 
 # magnitudes of the non-negative finite codes 0x00..0x7e, in code order

@@ -124,9 +124,10 @@ def _gate_up_bounds(a, off, wgu, a_scale, wsc, I):
     return A, dA
 
 
-def _assert_fp8_forward_close(got, ref, allowance, what):
+def _assert_fp8_forward_close(got, ref, inp, tokens, what):
     """Outputs outside the bf16 tolerance must be rare (at most 1 in 10^4)
-    and each within the code-decision allowance of its element: a code the
+    and each within the code-decision allowance of its element
+    (_forward_code_allowance, computed for the tokens concerned): a code the
     f32 error bound leaves open moves a few outputs of its token by about
     one large code step, while a wrong row or tile would move most of them."""
     excess = np.abs(got - ref) - (BF16_TOL[1] + BF16_TOL[0] * np.abs(ref))
@@ -135,7 +136,9 @@ def _assert_fp8_forward_close(got, ref, allowance, what):
     print(f"{what}: {n_bad} of {got.size} outputs outside the bf16 tolerance", flush=True)
     assert n_bad <= max(16, got.size // 10000), f"{what}: {n_bad} outputs out of tolerance"
     if n_bad:
-        over = excess[bad] - allowance[bad]
+        rows = np.nonzero(bad.any(axis=1))[0]
+        allowance = _forward_code_allowance(inp, np.asarray(tokens)[rows])
+        over = excess[rows][bad[rows]] - allowance[bad[rows]]
         assert (over <= 0).all(), (
             f"{what}: {int((over > 0).sum())} outputs beyond the code-decision allowance, "
             f"worst by {over.max():.3e}")
@@ -344,7 +347,7 @@ def test_forward_full_size_covering(dev, name, replicas):
     torch.cuda.synchronize()
     got = np64(out[torch.from_numpy(tokens).to(dev)].cpu())
     ref = _oracle(inp, tokens=tokens)
-    _assert_fp8_forward_close(got, ref, _forward_code_allowance(inp, tokens), name)
+    _assert_fp8_forward_close(got, ref, inp, tokens, name)
 
 
 def test_forward_many_items_per_block_all_tokens(dev):
@@ -377,8 +380,7 @@ def test_forward_many_items_per_block_all_tokens(dev):
     assert torch.equal(out.view(torch.int16), capped.view(torch.int16))
     assert torch.equal(out.view(torch.int16), staged.view(torch.int16))
     ref = _oracle(inp)
-    _assert_fp8_forward_close(np64(out.cpu()), ref,
-                              _forward_code_allowance(inp, np.arange(cfg.T)),
+    _assert_fp8_forward_close(np64(out.cpu()), ref, inp, np.arange(cfg.T),
                               "fp8 many items per block")
     assert rel_fro(np64(out.cpu()), ref) < 1e-2
 
