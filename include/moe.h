@@ -183,6 +183,25 @@ moe_status_t moe_slot_map(const int32_t* ids, const float* w, int T, int K, int 
 size_t moe_permute_workspace_size(int T, int K, int S);
 
 /*
+ * moe_permute_noalloc -- moe_permute without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).
+ * Arguments, outputs and errors as moe_permute. The per-chunk histograms
+ * live in a static device array of 65536 int32 (256 KiB), one per device,
+ * held until the process ends; every (T, K, S) that moe_permute accepts
+ * fits it (MOE_ERR_UNSUPPORTED otherwise). Its device address is looked up
+ * once per device, on the first call made while that device is current.
+ * Nothing in it needs clearing: each call writes every histogram entry it
+ * reads. All calls on one device share the array, so calls that may overlap
+ * on one device (different streams, or different host threads) race and
+ * must be ordered by the caller.
+ */
+moe_status_t moe_permute_noalloc(const void* x, moe_dtype_t dt, int T, int H, int K,
+                                 const int32_t* slot, const uint8_t* mask, int S,
+                                 int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_row,
+                                 void* x_perm, hipStream_t stream);
+
+/*
  * moe_permute_scaled -- moe_permute whose gathered rows carry the routing
  * weight: x_perm[pair_row[p]] = round(pair_w[p] * x[p / K]) (f32 product,
  * one rounding to dt), for input-side routing.

@@ -21,7 +21,8 @@ import torch
 __all__ = [
     "MOE_DTYPE_F32", "MOE_DTYPE_BF16", "GATE_UP_SWIGLU", "DOWN", "NUM_EVENTS",
     "lib", "library_path", "status_str",
-    "route", "slot_map", "permute", "permute_workspace_size", "grouped_gemm", "combine",
+    "route", "slot_map", "permute", "permute_noalloc", "permute_workspace_size",
+    "grouped_gemm", "combine",
     "forward", "forward_workspace_size", "ForwardConfig",
     "a2a_dispatch", "a2a_dispatch_workspace_size", "a2a_combine",
 ]
@@ -75,6 +76,7 @@ _SIGS = {
     "moe_permute": (_i, [_p, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_permute_scaled": (_i, [_p, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p, _p, _sz,
                                 _p]),
+    "moe_permute_noalloc": (_i, [_p, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p]),
     "moe_grouped_gemm": (_i, [_i, _i, _p, _p, _i, _i, _p, _i, _i, _p, _p]),
     "moe_combine": (_i, [_p, _i, _p, _p, _i, _i, _i, _p, _i, _i, _p]),
     "moe_combine_shared": (_i, [_p, _i, _p, _p, _i, _i, _i, _p, _i, _p, _i, _i, _p]),
@@ -237,6 +239,34 @@ def permute(x: torch.Tensor, slot: torch.Tensor, mask: torch.Tensor, S: int,
                                  _ptr(offsets), _ptr(sorted_pairs), _ptr(pair_row),
                                  _ptr(x_perm), _ptr(ws), ws.numel() * ws.element_size(),
                                  _stream()), "moe_permute")
+    return offsets, sorted_pairs, pair_row, x_perm
+
+
+def permute_noalloc(x: torch.Tensor, slot: torch.Tensor, mask: torch.Tensor, S: int,
+                    gather: bool = True, out=None):
+    """moe_permute_noalloc: moe_permute with the library's static histogram
+    memory (no workspace). `out` may pass preallocated (offsets, sorted_pairs,
+    pair_row, x_perm) so that the call itself allocates nothing."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    _dev(slot, "slot", torch.int32)
+    T, K = slot.shape
+    _dev(mask, "mask", torch.uint8, (T, K))
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be [T, H] with T matching slot")
+    H = x.shape[1]
+    if out is None:
+        out = (_empty((S + 1,), torch.int32, x), _empty((T * K,), torch.int32, x),
+               _empty((T * K,), torch.int32, x),
+               _empty((T * K, H), x.dtype, x) if gather else None)
+    offsets, sorted_pairs, pair_row, x_perm = out
+    _dev(offsets, "offsets", torch.int32, (S + 1,))
+    _dev(sorted_pairs, "sorted_pairs", torch.int32, (T * K,))
+    _dev(pair_row, "pair_row", torch.int32, (T * K,))
+    if x_perm is not None:
+        _dev(x_perm, "x_perm", x.dtype, (T * K, H))
+    _check(lib().moe_permute_noalloc(_ptr(x), _DT[x.dtype], T, H, K, _ptr(slot), _ptr(mask), S,
+                                     _ptr(offsets), _ptr(sorted_pairs), _ptr(pair_row),
+                                     _ptr(x_perm), _stream()), "moe_permute_noalloc")
     return offsets, sorted_pairs, pair_row, x_perm
 
 

@@ -287,6 +287,12 @@ struct PermutePlan {
   size_t ws_bytes;
 };
 PermutePlan permute_plan(int T, int K, int S);
+// Entries of the static histogram array behind moe_permute_noalloc (256 KiB
+// per device): permute_plan never needs more than 65536 / S chunks of S.
+constexpr int kPermuteScratchInts = 65536;
+// Device address of that array on the current device, looked up on the
+// first call per device (hipGetSymbolAddress) and kept for later calls.
+moe_status_t permute_scratch(int32_t** out);
 // seg_cap > 0 places slot s's rows in the fixed block [s * seg_cap,
 // (s + 1) * seg_cap) (the caller guarantees every slot fits). pair_w non-null:
 // the row of pair p is pair_w[p] * x[p / K] (f32 product, rounded once).

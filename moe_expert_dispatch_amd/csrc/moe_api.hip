@@ -274,6 +274,23 @@ moe_status_t moe_permute(const void* x, moe_dtype_t dt, int T, int H, int K,
                         pair_row, x_perm, ws, stream);
 }
 
+moe_status_t moe_permute_noalloc(const void* x, moe_dtype_t dt, int T, int H, int K,
+                                 const int32_t* slot, const uint8_t* mask, int S,
+                                 int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_row,
+                                 void* x_perm, hipStream_t stream) {
+  constexpr size_t kScratchBytes = (size_t)kPermuteScratchInts * sizeof(int32_t);
+  if (T < 0 || K < 1 || S < 1 || !pairs_fit(T, K)) return MOE_ERR_INVALID_ARG;
+  if (permute_plan(T, K, S).ws_bytes > kScratchBytes) return MOE_ERR_UNSUPPORTED;
+  int32_t* hist = nullptr;
+  moe_status_t st = permute_scratch(&hist);
+  if (st != MOE_OK) return st;
+  st = check_permute(x, dt, T, H, K, slot, mask, S, offsets, sorted_pairs, pair_row, x_perm,
+                     hist, kScratchBytes);
+  if (st != MOE_OK) return st;
+  return launch_permute(x, dtype_bytes(dt), T, H, K, slot, mask, S, offsets, sorted_pairs,
+                        pair_row, x_perm, hist, stream);
+}
+
 moe_status_t moe_permute_scaled(const void* x, moe_dtype_t dt, int T, int H, int K,
                                 const int32_t* slot, const uint8_t* mask, int S,
                                 const float* pair_w, int32_t* offsets, int32_t* sorted_pairs,

@@ -17,7 +17,16 @@
 //              the order inside a chunk is the pair order.
 //   4. gather  token-major: each token's row is read once and written to
 //              the K rows its included pairs occupy (16-byte vectors).
+#include <mutex>
+
 #include "common.h"
+
+// Histogram memory of moe_permute_noalloc: one static array per device
+// (each GPU the library runs on holds its own copy until the process ends).
+// 65536 entries cover every permutation the plan below admits (at most
+// 65536 / S chunks of S slots). In host code this name only stands for the
+// array: its device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) int32_t scratch[moe::kPermuteScratchInts];
 
 namespace moe {
 namespace {
@@ -357,6 +366,27 @@ PermutePlan permute_plan(int T, int K, int S) {
   // histograms, padded to whole 16-byte vectors for the scan
   pl.ws_bytes = ((size_t)S * (size_t)bound * sizeof(int32_t) + 15) / 16 * 16;
   return pl;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+}  // namespace
+
+moe_status_t permute_scratch(int32_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {  // first call on this device: it is current
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
