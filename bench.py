@@ -219,10 +219,19 @@ def cpu_baseline(inp, seconds, rank=0):
         el = time.perf_counter() - t0
         if el >= seconds or done >= cfg.T:
             break
+    host_cores = os.cpu_count() or 1
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = host_cores
+    # `cores` is the thread count the oracle ran with: numpy's BLAS threads
+    # (its matmuls); everything else in it is single-threaded numpy
     return {"value": done / el, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "host_cores": int(host_cores), "cores_usable": int(usable),
             "sample": (f"first {done} of {cfg.T} tokens of the same workload through the fp64 "
                        f"numpy oracle (route, EP mask / slot map, per-expert SwiGLU MLP, "
-                       f"combine), {el:.1f} s wall")}
+                       f"combine), {el:.1f} s wall; {int(blas_threads)} BLAS threads on a host "
+                       f"with {host_cores} logical cores ({usable} usable by this process)")}
 
 
 def main():

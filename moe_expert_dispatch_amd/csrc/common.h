@@ -64,6 +64,19 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return mx(b[0], b[1]);
 }
 
+// Integer sum over the wave by the same steps (exact, so every lane holds
+// the total).
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v += (int)dpp_u32<kDppQuad1032>((uint32_t)v);
+  v += (int)dpp_u32<kDppQuad2301>((uint32_t)v);
+  v += (int)dpp_u32<kDppRowHalfMirror>((uint32_t)v);
+  v += (int)dpp_u32<kDppRowMirror>((uint32_t)v);
+  const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = (int)a[0] + (int)a[1];
+  const auto b = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return (int)b[0] + (int)b[1];
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   auto dpp = [](float x, auto ctrl) {
     return __uint_as_float(dpp_u32<decltype(ctrl)::value>(__float_as_uint(x)));
@@ -282,7 +295,7 @@ struct FusedQuant {
 
 struct PermutePlan {
   int P;        // pairs
-  int chunk;    // pairs per chunk (multiple of 256)
+  int chunk;    // pairs per chunk: whole tokens (a multiple of K)
   int nchunks;  // ceil(P / chunk)
   size_t ws_bytes;
 };

@@ -6,17 +6,22 @@
 // experts, and the ragged gather that drops non-local pairs before compute.
 //
 // The result is a pure function of (slot, mask): within a slot, pairs keep
-// ascending pair index. Four kernels, all deterministic:
-//   1. count   one block per chunk of pairs: LDS histogram over slots,
-//              written slot-major: hist[s * nchunks + c].
-//   2. scan    one block, one pass: exclusive scan of hist in slot-major
-//              order, which yields each (slot, chunk) base row;
-//              offsets[s] = base of (s, chunk 0) and offsets[S] = P_in.
-//   3. scatter one block per chunk: batches of 64 pairs are ranked with a
-//              ballot per slot and per-batch counts are scanned in LDS, so
-//              the order inside a chunk is the pair order.
-//   4. gather  token-major: each token's row is read once and written to
-//              the K rows its included pairs occupy (16-byte vectors).
+// ascending pair index. Chunks are runs of whole tokens. Two launches, both
+// deterministic:
+//   1. count   one block per chunk: LDS histogram over slots, written
+//              slot-major: hist[s * nchunks + c].
+//   2. rank    one block per chunk. The block derives its own base rows from
+//              all histograms (slot totals, their exclusive scan over slots,
+//              plus the counts of the earlier chunks of each slot; chunk 0
+//              also writes offsets), so no separate scan launch sits between
+//              the two. Batches of 64 pairs are then ranked with a ballot
+//              per slot and per-batch counts scanned in LDS, so the order
+//              inside a chunk is the pair order. With the row gather, the
+//              block keeps its pairs' rows in LDS and copies each of its
+//              tokens' hidden row once from x to the rows its included
+//              pairs occupy (16-byte vectors, one wave per token).
+// A chunk too long for its rows to fit in LDS runs the gather as a third,
+// token-major launch instead.
 #include <mutex>
 
 #include "common.h"
@@ -60,46 +65,69 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
   for (int i = threadIdx.x; i < S; i += blockDim.x) hist[(size_t)i * nchunks + c] = lds_hist[i];
 }
 
-constexpr int kScanThreads = 1024;
-constexpr int kScanVec = 16;  // 16-byte vectors per thread: 64 entries, and
-                              // S * nchunks <= 65536 (permute_plan)
+constexpr int kRankThreads = 512;  // 8 waves: one batch of 64 pairs each per sub-chunk
+constexpr int kRankWaves = kRankThreads / kWave;
+static_assert(kBatches == kRankWaves, "one batch per wave");
+constexpr int kBaseRows = 8;  // histogram rows a wave sums at a time ...
+constexpr int kBaseCols = 4;  // ... and 64-entry column blocks of each, all loads in flight
 
-// Exclusive scan of hist[0..N) in place, N = S * nchunks, in one pass: thread
-// t owns the contiguous entries [t * per, (t + 1) * per) (per a multiple of 4,
-// at most 64), loads them with up to 16 vector loads all in flight, and one
-// block scan of the per-thread sums gives every thread its base. The
-// workspace is padded to whole vectors; entries at or past N count as 0 and
-// are not written.
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict__ hist, int S,
-                                                            int nchunks,
-                                                            int32_t* __restrict__ offsets) {
-  __shared__ int32_t wsum[kScanThreads / kWave];
-  const int N = S * nchunks;
-  const int per = 4 * ceil_div(N, 4 * kScanThreads);
+// Base rows of chunk c, from the per-chunk histograms hist[s * nchunks + j]
+// (counts): tot[s] = sum over j of hist[s][j], pre[s] = sum over j < c;
+// the slot's first row is the exclusive scan of tot over slots (or s *
+// seg_cap for fixed-capacity blocks). running[s] = first row + pre[s].
+// Chunk 0 writes offsets[s] (the scan) and offsets[S] (all included pairs).
+// tot and wsum are LDS scratch ([S], [kRankWaves]).
+__device__ __forceinline__ void chunk_bases(const int32_t* __restrict__ hist, int S, int nchunks,
+                                            int c, int seg_cap, int32_t* running, int32_t* tot,
+                                            int32_t* wsum, int32_t* __restrict__ offsets) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
-  const int lo = tid * per;
-  int4 q[kScanVec];
+  // wave w sums rows s = w, w + 8, ... (kBaseRows rows at a time); lane l
+  // reads entries j = l, l + 64, ... of each (kBaseCols per row at a time),
+  // so each step has kBaseRows * kBaseCols loads in flight
+  const int rows_w = wave < S ? ceil_div(S - wave, kRankWaves) : 0;
+  for (int r0 = 0; r0 < rows_w; r0 += kBaseRows) {
+    int tsum[kBaseRows], psum[kBaseRows];
 #pragma unroll
-  for (int k = 0; k < kScanVec; ++k) {
-    const int i = lo + 4 * k;
-    q[k] = (4 * k < per && i < N) ? *reinterpret_cast<const int4*>(hist + i)
-                                   : make_int4(0, 0, 0, 0);
-  }
-  int sum = 0;
+    for (int i = 0; i < kBaseRows; ++i) tsum[i] = psum[i] = 0;
+    for (int j0 = 0; j0 < nchunks; j0 += kBaseCols * kWave) {
+      int v[kBaseRows][kBaseCols];
 #pragma unroll
-  for (int k = 0; k < kScanVec; ++k) {
-    const int i = lo + 4 * k;
-    const bool in = 4 * k < per;
-    q[k].x = in && i < N ? q[k].x : 0;
-    q[k].y = in && i + 1 < N ? q[k].y : 0;
-    q[k].z = in && i + 2 < N ? q[k].z : 0;
-    q[k].w = in && i + 3 < N ? q[k].w : 0;
-    sum += q[k].x + q[k].y + q[k].z + q[k].w;
+      for (int i = 0; i < kBaseRows; ++i) {
+        const int srow = wave + kRankWaves * (r0 + i);
+#pragma unroll
+        for (int m = 0; m < kBaseCols; ++m) {
+          const int j = j0 + m * kWave + lane;
+          v[i][m] = (r0 + i < rows_w && j < nchunks) ? hist[(size_t)srow * nchunks + j] : 0;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kBaseRows; ++i) {
+#pragma unroll
+        for (int m = 0; m < kBaseCols; ++m) {
+          tsum[i] += v[i][m];
+          psum[i] += j0 + m * kWave + lane < c ? v[i][m] : 0;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBaseRows; ++i) {
+      const int t = wave_sum_i32(tsum[i]);
+      const int q = wave_sum_i32(psum[i]);
+      if (lane == 0 && r0 + i < rows_w) {
+        const int srow = wave + kRankWaves * (r0 + i);
+        tot[srow] = t;
+        running[srow] = q;
+      }
+    }
   }
-  // inclusive scan of the per-thread sums: within the wave, then across waves
-  int incl = sum;
+  __syncthreads();
+  // exclusive scan of tot over the slots: thread t owns slots 2t, 2t + 1
+  // (S <= 1024 = 2 * kRankThreads)
+  const int a = 2 * tid < S ? tot[2 * tid] : 0;
+  const int b = 2 * tid + 1 < S ? tot[2 * tid + 1] : 0;
+  int incl = a + b;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
     const int o = __shfl_up(incl, off, kWave);
@@ -107,145 +135,114 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict_
   }
   if (lane == kWave - 1) wsum[wave] = incl;
   __syncthreads();
-  if (wave == 0) {
-    int w = lane < kScanThreads / kWave ? wsum[lane] : 0;
-#pragma unroll
-    for (int off = 1; off < kScanThreads / kWave; off <<= 1) {
-      const int o = __shfl_up(w, off, kWave);
-      if (lane >= off) w += o;
-    }
-    if (lane < kScanThreads / kWave) wsum[lane] = w;
+  int before = 0, total = 0;
+  for (int w = 0; w < kRankWaves; ++w) {
+    before += w < wave ? wsum[w] : 0;
+    total += wsum[w];
   }
+  const int first = before + incl - (a + b);  // first row of slot 2t
+  if (2 * tid < S) {
+    const int r0 = seg_cap > 0 ? 2 * tid * seg_cap : first;
+    running[2 * tid] += r0;
+    if (c == 0) offsets[2 * tid] = first;
+  }
+  if (2 * tid + 1 < S) {
+    const int r1 = seg_cap > 0 ? (2 * tid + 1) * seg_cap : first + a;
+    running[2 * tid + 1] += r1;
+    if (c == 0) offsets[2 * tid + 1] = first + a;
+  }
+  if (c == 0 && tid == 0) offsets[S] = total;
   __syncthreads();
-  int run = incl - sum + (wave > 0 ? wsum[wave - 1] : 0);
-#pragma unroll
-  for (int k = 0; k < kScanVec; ++k) {
-    const int i = lo + 4 * k;
-    if (4 * k < per && i < N) {
-      int4 e;
-      e.x = run;
-      e.y = e.x + q[k].x;
-      e.z = e.y + q[k].y;
-      e.w = e.z + q[k].z;
-      run = e.w + q[k].w;
-      if (i + 3 < N) {
-        *reinterpret_cast<int4*>(hist + i) = e;
-      } else {
-        hist[i] = e.x;
-        if (i + 1 < N) hist[i + 1] = e.y;
-        if (i + 2 < N) hist[i + 2] = e.z;
-      }
-    }
-  }
-  __syncthreads();  // the scanned entries are visible to the whole block
-  for (int s = tid; s < S; s += kScanThreads)
-    offsets[s] = nchunks > 0 ? hist[(size_t)s * nchunks] : 0;
-  if (tid == 0) offsets[S] = wsum[kScanThreads / kWave - 1];
 }
 
-// One block (4 waves) per chunk. The chunk is walked in sub-chunks of 512
-// pairs = 8 batches of 64; wave w ranks batches 2w and 2w+1. Inside a batch the
-// lanes holding the same slot are ranked with a ballot (lane order = pair
-// order); per-batch slot counts, scanned over the batches, give each batch's
-// base row, so the order inside a slot is the pair order.
+// Ranking and scatter of chunk c (one block of kRankThreads). The chunk is
+// walked in sub-chunks of 512 pairs = 8 batches of 64, one per wave. Inside a
+// batch the lanes holding the same slot are ranked with a ballot (lane order
+// = pair order); per-batch slot counts, scanned over the batches, give each
+// batch's base row, so the order inside a slot is the pair order.
 // seg_cap > 0: slot s's rows start at s * seg_cap instead of offsets[s]
-// (fixed-capacity blocks, one per slot).
-__device__ __forceinline__ void scatter_chunk(int c, const int32_t* __restrict__ slot,
-                                              const uint8_t* __restrict__ mask, int P, int S,
-                                              int chunk, int nchunks,
-                                              const int32_t* __restrict__ base,
-                                              const int32_t* __restrict__ offsets, int seg_cap,
-                                              int32_t* __restrict__ sorted_pairs,
-                                              int32_t* __restrict__ pair_row) {
+// (fixed-capacity blocks, one per slot). rows_lds non-null: the rows of the
+// chunk's pairs are also kept there (index p - c * chunk).
+__device__ __forceinline__ void rank_chunk(int c, const int32_t* __restrict__ slot,
+                                           const uint8_t* __restrict__ mask, int P, int S,
+                                           int chunk, int nchunks,
+                                           const int32_t* __restrict__ hist,
+                                           int32_t* __restrict__ offsets, int seg_cap,
+                                           int32_t* __restrict__ sorted_pairs,
+                                           int32_t* __restrict__ pair_row, int32_t* rows_lds) {
   extern __shared__ int32_t lds[];
-  int32_t* running = lds;       // [S] next free row per slot
-  int32_t* bcount = lds + S;    // [kBatches][S] counts, then base rows
+  int32_t* running = lds;            // [S] next free row per slot
+  int32_t* tot = lds + S;            // [S] slot totals (base computation)
+  int32_t* bcount = lds + 2 * S;     // [kBatches][S] counts, then base rows
+  int32_t* wsum = lds + (2 + kBatches) * S;  // [kRankWaves]
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
-  for (int i = tid; i < S; i += blockDim.x) running[i] = base[(size_t)i * nchunks + c];
+  chunk_bases(hist, S, nchunks, c, seg_cap, running, tot, wsum, offsets);
   const int p0 = c * chunk;
   const int p1 = min(p0 + chunk, P);
   for (int q0 = p0; q0 < p1; q0 += kSub) {
-    for (int i = tid; i < kBatches * S; i += blockDim.x) bcount[i] = 0;
+    for (int i = tid; i < kBatches * S; i += kRankThreads) bcount[i] = 0;
     __syncthreads();
-    constexpr int kPer = kBatches / 4;  // batches per wave
-    int s[kPer], rank[kPer];
-    bool inc[kPer];
-#pragma unroll
-    for (int m = 0; m < kPer; ++m) {
-      const int p = q0 + (wave * kPer + m) * kWave + lane;
-      s[m] = -1;
-      inc[m] = p < p1 && included(slot, mask, p, P, S, &s[m]);
-    }
-#pragma unroll
-    for (int m = 0; m < kPer; ++m) {
-      const int b = wave * kPer + m;
-      rank[m] = 0;
-      uint64_t active = __ballot(inc[m]);
-      while (active) {
-        const int leader = __ffsll((unsigned long long)active) - 1;
-        const int ls = __shfl(s[m], leader, kWave);
-        const uint64_t same = __ballot(inc[m] && s[m] == ls);
-        if (inc[m] && s[m] == ls) rank[m] = __popcll(same & lanemask_lt());
-        if (lane == leader) bcount[b * S + ls] = __popcll(same);
-        active &= ~same;
-      }
+    const int b = wave;  // this wave's batch
+    const int p = q0 + b * kWave + lane;
+    int s = -1;
+    const bool inc = p < p1 && included(slot, mask, p, P, S, &s);
+    int rank = 0;
+    uint64_t active = __ballot(inc);
+    while (active) {
+      const int leader = __ffsll((unsigned long long)active) - 1;
+      const int ls = __shfl(s, leader, kWave);
+      const uint64_t same = __ballot(inc && s == ls);
+      if (inc && s == ls) rank = __popcll(same & lanemask_lt());
+      if (lane == leader) bcount[b * S + ls] = __popcll(same);
+      active &= ~same;
     }
     __syncthreads();
-    for (int i = tid; i < S; i += blockDim.x) {
+    for (int i = tid; i < S; i += kRankThreads) {
       int run = running[i];
-      for (int b = 0; b < kBatches; ++b) {
-        const int t = bcount[b * S + i];
-        bcount[b * S + i] = run;
+      for (int bb = 0; bb < kBatches; ++bb) {
+        const int t = bcount[bb * S + i];
+        bcount[bb * S + i] = run;
         run += t;
       }
       running[i] = run;
     }
     __syncthreads();
-#pragma unroll
-    for (int m = 0; m < kPer; ++m) {
-      const int b = wave * kPer + m;
-      const int p = q0 + b * kWave + lane;
-      if (p < p1) {
-        int row = inc[m] ? bcount[b * S + s[m]] + rank[m] : -1;
-        if (seg_cap > 0 && row >= 0) row += s[m] * seg_cap - offsets[s[m]];
-        pair_row[p] = row;
-        if (row >= 0) sorted_pairs[row] = p;
-      }
+    if (p < p1) {
+      const int row = inc ? bcount[b * S + s] + rank : -1;
+      pair_row[p] = row;
+      if (row >= 0) sorted_pairs[row] = p;
+      if (rows_lds) rows_lds[p - p0] = row;
     }
     __syncthreads();
   }
 }
 
-__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ slot,
-                                                      const uint8_t* __restrict__ mask, int P,
-                                                      int S, int chunk, int nchunks,
-                                                      const int32_t* __restrict__ base,
-                                                      const int32_t* __restrict__ offsets,
-                                                      int seg_cap,
-                                                      int32_t* __restrict__ sorted_pairs,
-                                                      int32_t* __restrict__ pair_row) {
-  scatter_chunk(blockIdx.x, slot, mask, P, S, chunk, nchunks, base, offsets, seg_cap,
-                sorted_pairs, pair_row);
+__global__ __launch_bounds__(kRankThreads) void rank_kernel(
+    const int32_t* __restrict__ slot, const uint8_t* __restrict__ mask, int P, int S, int chunk,
+    int nchunks, const int32_t* __restrict__ hist, int32_t* __restrict__ offsets, int seg_cap,
+    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_row) {
+  rank_chunk(blockIdx.x, slot, mask, P, S, chunk, nchunks, hist, offsets, seg_cap, sorted_pairs,
+             pair_row, nullptr);
 }
 
-// The scatter with a quantization riding along: blocks [0, nchunks) scatter
+// The ranking with a quantization riding along: blocks [0, rblocks) rank
 // their chunk, the remaining blocks quantize 16 values per thread. The two
 // are independent, so the quantization's HBM traffic overlaps the
-// latency-bound scatter instead of following it. The branch is uniform per
-// block, so the scatter's barriers are reached by whole blocks.
-__global__ __launch_bounds__(256) void scatter_quant_kernel(
+// latency-bound ranking instead of following it. The branch is uniform per
+// block, so the ranking's barriers are reached by whole blocks.
+__global__ __launch_bounds__(kRankThreads) void rank_quant_kernel(
     const int32_t* __restrict__ slot, const uint8_t* __restrict__ mask, int P, int S, int chunk,
-    int nchunks, const int32_t* __restrict__ base, const int32_t* __restrict__ offsets,
+    int nchunks, int rblocks, const int32_t* __restrict__ hist, int32_t* __restrict__ offsets,
     int seg_cap, int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_row,
     FusedQuant fq) {
-  if ((int)blockIdx.x < nchunks)
-    scatter_chunk(blockIdx.x, slot, mask, P, S, chunk, nchunks, base, offsets, seg_cap,
-                  sorted_pairs, pair_row);
+  if ((int)blockIdx.x < rblocks)
+    rank_chunk(blockIdx.x, slot, mask, P, S, chunk, nchunks, hist, offsets, seg_cap,
+               sorted_pairs, pair_row, nullptr);
   else
     quantize16(fq.x, fq.n, fq.inv, fq.q,
-               (int64_t)(blockIdx.x - (unsigned)nchunks) * blockDim.x + threadIdx.x);
+               (int64_t)(blockIdx.x - (unsigned)rblocks) * blockDim.x + threadIdx.x);
 }
 
 typedef int int32x4_t __attribute__((ext_vector_type(4)));
@@ -350,20 +347,99 @@ __global__ __launch_bounds__(256) void gather_scaled_kernel(const uint4* __restr
   gather_rows<true, ET>(x + (size_t)t * nvec, nvec, K, rows, ws, x_perm);
 }
 
+// Ranking of chunk c followed by the row gather of its tokens, one wave per
+// token (tokens t0 + w, t0 + w + 8, ...): the token's row is loaded
+// (kWaveVec 16-byte vectors per lane at a time, all in flight) and stored to
+// the rows its included pairs occupy, which the ranking left in LDS.
+constexpr int kWaveVec = 8;
+constexpr size_t kMaxRankLds = 65536;  // bytes of dynamic LDS a ranking block may use
+
+template <bool SCALED, typename ET>
+__global__ __launch_bounds__(kRankThreads) void rank_gather_kernel(
+    const int32_t* __restrict__ slot, const uint8_t* __restrict__ mask, int P, int S, int chunk,
+    int nchunks, const int32_t* __restrict__ hist, int32_t* __restrict__ offsets, int seg_cap,
+    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_row,
+    const uint4* __restrict__ x, int nvec, int K, const float* __restrict__ pair_w,
+    uint4* __restrict__ x_perm) {
+  extern __shared__ int32_t lds[];
+  const int c = blockIdx.x;
+  int32_t* rows_lds = lds + (2 + kBatches) * S + kRankWaves;
+  rank_chunk(c, slot, mask, P, S, chunk, nchunks, hist, offsets, seg_cap, sorted_pairs,
+             pair_row, rows_lds);  // ends with a barrier: rows_lds is complete
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int tpc = chunk / K;
+  const int t0 = c * tpc;
+  const int t1 = min(t0 + tpc, P / K);
+  const uint32_t row_bytes = (uint32_t)nvec * 16u;
+  auto load_row = [&](int t, int v0, int32x4_t* val) {
+    const __amdgpu_buffer_rsrc_t sr = row_rsrc(x + (size_t)t * nvec, row_bytes);
+#pragma unroll
+    for (int u = 0; u < kWaveVec; ++u) {
+      const int v = v0 + u * kWave;
+      val[u] = __builtin_amdgcn_raw_buffer_load_b128(sr, v < nvec ? (uint32_t)v * 16u : row_bytes,
+                                                     0, 0);
+    }
+  };
+  auto store_rows = [&](int t, int v0, const int32x4_t* val) {
+    for (int k = 0; k < K; ++k) {
+      const int r = rows_lds[(t - t0) * K + k];
+      if (r < 0) continue;  // wave-uniform
+      float wk = 1.0f;
+      if constexpr (SCALED) wk = pair_w[(size_t)t * K + k];
+      const __amdgpu_buffer_rsrc_t dr = row_rsrc(x_perm + (size_t)r * nvec, row_bytes);
+#pragma unroll
+      for (int u = 0; u < kWaveVec; ++u) {
+        const int v = v0 + u * kWave;
+        int32x4_t o = val[u];
+        if constexpr (SCALED) o = scale_row(o, wk, (const ET*)nullptr);
+        __builtin_amdgcn_raw_buffer_store_b128(o, dr, v < nvec ? (uint32_t)v * 16u : row_bytes,
+                                               0, kNonTemporal);
+      }
+    }
+  };
+  if (nvec <= kWaveVec * kWave) {
+    // a row is one load step: the wave's next token is loaded while the
+    // current one is stored
+    int32x4_t cur[kWaveVec], nxt[kWaveVec];
+    int t = t0 + wave;
+    if (t < t1) load_row(t, lane, cur);
+    for (; t < t1; t += kRankWaves) {
+      const bool more = t + kRankWaves < t1;  // wave-uniform
+      if (more) load_row(t + kRankWaves, lane, nxt);
+      store_rows(t, lane, cur);
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < kWaveVec; ++u) cur[u] = nxt[u];
+      }
+    }
+  } else {
+    for (int t = t0 + wave; t < t1; t += kRankWaves) {
+      for (int v0 = lane; v0 < nvec; v0 += kWaveVec * kWave) {
+        int32x4_t val[kWaveVec];
+        load_row(t, v0, val);
+        store_rows(t, v0, val);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 PermutePlan permute_plan(int T, int K, int S) {
   PermutePlan pl;
   pl.P = T * K;
-  // At most max(1, 65536 / S) chunks, so the scan stays small; chunks are
-  // whole sub-chunks of 512 pairs.
+  // About one chunk per 512 pairs, at most max(1, 65536 / S) chunks (so the
+  // histograms stay small: each ranking block reads all of them); a chunk is
+  // a run of whole tokens, so the block that ranks it can also gather them.
   const int cap = S > 0 ? (65536 / S > 0 ? 65536 / S : 1) : 1;
   const int units = ceil_div(pl.P, kSub);
   const int n = units < cap ? units : cap;
-  pl.chunk = kSub * (n > 0 ? ceil_div(units, n) : 1);
-  pl.nchunks = pl.P > 0 ? ceil_div(pl.P, pl.chunk) : 0;
+  const int tokens = n > 0 ? ceil_div(T, n) : 1;  // tokens per chunk
+  pl.chunk = tokens * K;
+  pl.nchunks = pl.P > 0 ? ceil_div(T, tokens) : 0;  // <= n
   const int bound = n > 0 ? n : 1;  // min(units, cap), monotone in P
-  // histograms, padded to whole 16-byte vectors for the scan
+  // histograms, padded to whole 16-byte vectors
   pl.ws_bytes = ((size_t)S * (size_t)bound * sizeof(int32_t) + 15) / 16 * 16;
   return pl;
 }
@@ -395,33 +471,45 @@ moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
                             hipStream_t stream, int seg_cap, const float* pair_w,
                             const FusedQuant* quant) {
   const PermutePlan pl = permute_plan(T, K, S);
-  // the one-pass scan covers up to 64 entries per thread
-  if ((long long)S * pl.nchunks > (long long)kScanThreads * 4 * kScanVec)
-    return MOE_ERR_UNSUPPORTED;
   int32_t* hist = static_cast<int32_t*>(ws);
-  const size_t lds = (size_t)S * sizeof(int32_t);
   if (pl.nchunks > 0) {
-    count_kernel<<<pl.nchunks, 256, lds, stream>>>(slot, mask, pl.P, S, pl.chunk, pl.nchunks,
-                                                  hist);
+    count_kernel<<<pl.nchunks, 256, (size_t)S * sizeof(int32_t), stream>>>(
+        slot, mask, pl.P, S, pl.chunk, pl.nchunks, hist);
   }
-  scan_kernel<<<1, kScanThreads, 0, stream>>>(hist, S, pl.nchunks, offsets);
-  const int64_t qblocks =
-      (quant != nullptr && quant->n > 0) ? ((quant->n + 15) / 16 + 255) / 256 : 0;
-  if (pl.nchunks > 0 || qblocks > 0) {
-    const size_t lds_scatter = (size_t)(1 + kBatches) * S * sizeof(int32_t);
-    if (qblocks > 0)
-      scatter_quant_kernel<<<(unsigned)(pl.nchunks + qblocks), 256, lds_scatter, stream>>>(
-          slot, mask, pl.P, S, pl.chunk, pl.nchunks, hist, offsets, seg_cap, sorted_pairs,
-          pair_row, *quant);
-    else
-      scatter_kernel<<<pl.nchunks, 256, lds_scatter, stream>>>(slot, mask, pl.P, S, pl.chunk,
-                                                              pl.nchunks, hist, offsets,
-                                                              seg_cap, sorted_pairs, pair_row);
+  // at least one ranking block: chunk 0 writes offsets (all zero when empty)
+  const int rblocks = pl.nchunks > 0 ? pl.nchunks : 1;
+  const size_t lds_rank = ((size_t)(2 + kBatches) * S + kRankWaves) * sizeof(int32_t);
+  const size_t lds_fused = lds_rank + (size_t)pl.chunk * sizeof(int32_t);
+  const int nvec = H * elem_bytes / 16;
+  const uint4* x4 = static_cast<const uint4*>(x);
+  uint4* xp4 = static_cast<uint4*>(x_perm);
+  const bool gather = x_perm != nullptr && T > 0;
+  const bool fused = gather && lds_fused <= kMaxRankLds;
+  const int64_t qblocks = (quant != nullptr && quant->n > 0)
+                              ? ((quant->n + 15) / 16 + kRankThreads - 1) / kRankThreads
+                              : 0;
+  if (qblocks > 0) {
+    rank_quant_kernel<<<(unsigned)(rblocks + qblocks), kRankThreads, lds_rank, stream>>>(
+        slot, mask, pl.P, S, pl.chunk, pl.nchunks, rblocks, hist, offsets, seg_cap,
+        sorted_pairs, pair_row, *quant);
+  } else if (fused && pair_w == nullptr) {
+    rank_gather_kernel<false, uint16_t><<<rblocks, kRankThreads, lds_fused, stream>>>(
+        slot, mask, pl.P, S, pl.chunk, pl.nchunks, hist, offsets, seg_cap, sorted_pairs,
+        pair_row, x4, nvec, K, nullptr, xp4);
+  } else if (fused && elem_bytes == 2) {
+    rank_gather_kernel<true, uint16_t><<<rblocks, kRankThreads, lds_fused, stream>>>(
+        slot, mask, pl.P, S, pl.chunk, pl.nchunks, hist, offsets, seg_cap, sorted_pairs,
+        pair_row, x4, nvec, K, pair_w, xp4);
+  } else if (fused) {
+    rank_gather_kernel<true, float><<<rblocks, kRankThreads, lds_fused, stream>>>(
+        slot, mask, pl.P, S, pl.chunk, pl.nchunks, hist, offsets, seg_cap, sorted_pairs,
+        pair_row, x4, nvec, K, pair_w, xp4);
+  } else {
+    rank_kernel<<<rblocks, kRankThreads, lds_rank, stream>>>(slot, mask, pl.P, S, pl.chunk,
+                                                             pl.nchunks, hist, offsets, seg_cap,
+                                                             sorted_pairs, pair_row);
   }
-  if (x_perm != nullptr && T > 0) {
-    const int nvec = H * elem_bytes / 16;
-    const uint4* x4 = static_cast<const uint4*>(x);
-    uint4* xp4 = static_cast<uint4*>(x_perm);
+  if (gather && !fused) {  // chunks too long for their rows to stay in LDS
     if (pair_w == nullptr)
       gather_kernel<<<T, 256, 0, stream>>>(x4, T, nvec, K, pair_row, xp4);
     else if (elem_bytes == 2)
