@@ -448,7 +448,10 @@ typedef int int32x2_t __attribute__((ext_vector_type(2)));
 // 64-wide bf16 slice, so stages, DMA and swizzle are shared; a slice is two
 // k-blocks of v_mfma_f32_32x32x64_f8f6f4, each lane holding 32 bytes (two
 // 16-byte chunks) of a row.
-template <int OP, bool GATHER, bool FP8>
+// XP: the cross-item prefetch (bf16 only; the launcher selects it when the
+// number of 64-wide K-slices is even and at least 4). Kept a template
+// parameter: one kernel holding both item schedules spills.
+template <int OP, bool GATHER, bool FP8, bool XP = false>
 __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
     const uint4* __restrict__ A, const int32_t* __restrict__ offsets, int S,
     const uint4* __restrict__ W, int N, int Kd, void* __restrict__ C,
@@ -655,18 +658,24 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
   // except in the gathered bf16 gate/up kernel, whose SwiGLU epilogue has no
   // registers left for it.
   constexpr bool EARLY = !(GATHER && !FP8);
-  auto issue_next = [&](const WItem& x, auto before_epilogue) {
+  // xp: the next item's slice 0 (and, except with the staged epilogue,
+  // slice 1) was already requested by the last K-slices of this item.
+  auto issue_next = [&](const WItem& x, auto before_epilogue, bool xp) {
     if constexpr (decltype(before_epilogue)::value) {
       if constexpr (EARLY) {
-        gather_offsets(cur);
-        issue_slice(x, 0);
+        if (!xp) {
+          gather_offsets(cur);
+          issue_slice(x, 0);
+        }
       }
     } else {
       if constexpr (!EARLY) {
-        gather_offsets(cur);
-        issue_slice(x, 0);
+        if (!xp) {
+          gather_offsets(cur);
+          issue_slice(x, 0);
+        }
       }
-      issue_slice(x, 1);
+      if (!xp || STAGED) issue_slice(x, 1);
     }
   };
   auto epilogue_down = [&](const WItem& x) {
@@ -790,7 +799,11 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
   auto lgkm_wait = [&](auto nc, bf16x8_t& wb, bf16x8_t& wa) {
     asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(wb), "+v"(wa) : "n"(decltype(nc)::value));
   };
-  auto dstep = [&](int d, auto first, auto chk, auto nic) {
+  // Block 3 of slice d requests slice fd (d + 2 inside an item; with the
+  // cross-item prefetch the next item's slice 0 or 1) into stage fd & 1;
+  // `go` converts the next item's gathered row indices first (their loads
+  // were drained by this slice's full wait).
+  auto dstep = [&](int d, auto first, auto chk, auto nic, int fd, bool go) {
     constexpr int NI = decltype(nic)::value;
     constexpr int NX = NI == 4 ? 8 : 4;  // MFMAs per K-16 block
     constexpr int NR = frag_reads<NI>();  // fragment reads per K-16 block
@@ -847,16 +860,23 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
     wait_frags(f1a, f1b);
     vm_wait<0>();
     __builtin_amdgcn_s_barrier();
+    if constexpr (GATHER) {
+      if (go) {
+        __builtin_amdgcn_sched_barrier(0);
+        gather_offsets(cur);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
 #pragma unroll
     for (int y = 0; y < NX; ++y) {
       if constexpr (OP == 0) {
         mfma1(xm(y), f1a, f1b);
-        dma(cur, (8 / NX) * y, d + 2, decltype(chk)::value);
-        if constexpr (NX == 4) dma(cur, 2 * y + 1, d + 2, decltype(chk)::value);
+        dma(cur, (8 / NX) * y, fd, decltype(chk)::value);
+        if constexpr (NX == 4) dma(cur, 2 * y + 1, fd, decltype(chk)::value);
         if (y < NR) read8(frag_read_order<NI>(y), f0a, f0b, nbase + a_lane[0], nbase + b_lane[0]);
       } else {
-        dma(cur, (8 / NX) * y, d + 2, decltype(chk)::value);
-        if constexpr (NX == 4) dma(cur, 2 * y + 1, d + 2, decltype(chk)::value);
+        dma(cur, (8 / NX) * y, fd, decltype(chk)::value);
+        if constexpr (NX == 4) dma(cur, 2 * y + 1, fd, decltype(chk)::value);
         if (NI == 4 ? y < 6 : true) read8(xm(y), f0a, f0b, nbase + a_lane[0], nbase + b_lane[0]);
         mfma1(xm(y), f1a, f1b);
       }
@@ -963,11 +983,14 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
   // A slice for waves whose rows are all padding (the lower 128 rows of an
   // item with at most 128 rows): only their share of the operand DMAs and
   // the barrier, no fragment reads or MFMAs.
-  auto pass_step = [&](int d) {
+  auto pass_step = [&](int fd, bool go) {
     vm_wait<0>();
     __builtin_amdgcn_s_barrier();
+    if constexpr (GATHER) {
+      if (go) gather_offsets(cur);
+    }
 #pragma unroll
-    for (int x = 0; x < 8; ++x) dma(cur, x, d + 2);
+    for (int x = 0; x < 8; ++x) dma(cur, x, fd);
   };
 
   int rt, ct;
@@ -990,11 +1013,19 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
       has_next = nxt < total;
       if (has_next) setup(rt, ct, cur);
     };
-    // With the gather, the next item is set up before the last slice, whose
-    // full wait then covers setup's index loads: they have completed before
-    // any epilogue store is issued. (A store can complete before an older
-    // load, so no wait may count across the stores.) The last slice's DMAs
-    // are out of range whatever item they name.
+    // Cross-item prefetch (bf16, an even number of K-slices, at least 4):
+    // the next item is set up before the second-to-last slice, whose block 3
+    // requests the next item's slice 0 into stage 0 instead of an
+    // out-of-range slice; the last slice requests its slice 1 into stage 1,
+    // except with the staged down epilogue, which needs stage 1 (it is then
+    // requested after the epilogue as before). The next item's gathered row
+    // indices are converted after the second-to-last slice's full wait.
+    constexpr bool xp = XP && !FP8;
+    // Without it: with the gather, the next item is set up before the last
+    // slice, whose full wait then covers setup's index loads: they have
+    // completed before any epilogue store is issued. (A store can complete
+    // before an older load, so no wait may count across the stores.) The
+    // last slice's DMAs are out of range whatever item they name.
     const int dlast = GATHER ? nd - 1 : nd;
     // The epilogue sits inside the computing branch, so the accumulators are
     // not live across the pass-only slices.
@@ -1021,6 +1052,7 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
       } else {
         const std::true_type checked;
         const std::false_type unchecked;
+        const std::false_type later;
         auto kloop = [&](auto nic) {
           constexpr int NI = decltype(nic)::value;
           if constexpr (NI == 2) {  // padding rows: defined, never stored
@@ -1035,14 +1067,21 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
                                   : (NI == 4 ? y : ((y & 1) | ((y >> 1) << 2)));
             read8(x, f0a, f0b, smem_base + a_lane[0], smem_base + b_lane[0]);
           }
-          dstep(0, std::true_type{}, checked, nic);
+          dstep(0, std::true_type{}, checked, nic, 2, false);
           // the DMA of slice d + 2 is in range for d < nd - 2
           int d = 1;
-          for (; d < dlast && d < nd - 2; ++d) dstep(d, std::false_type{}, unchecked, nic);
-          for (; d < dlast; ++d) dstep(d, std::false_type{}, checked, nic);
-          if constexpr (GATHER) {
+          if constexpr (xp) {
+            for (; d < nd - 2; ++d) dstep(d, later, unchecked, nic, d + 2, false);
             next_setup();
-            dstep(nd - 1, std::false_type{}, checked, nic);
+            dstep(nd - 2, later, checked, nic, has_next ? 0 : nd, has_next);
+            dstep(nd - 1, later, checked, nic, has_next && !STAGED ? 1 : nd + 1, false);
+          } else {
+            for (; d < dlast && d < nd - 2; ++d) dstep(d, later, unchecked, nic, d + 2, false);
+            for (; d < dlast; ++d) dstep(d, later, checked, nic, d + 2, false);
+            if constexpr (GATHER) {
+              next_setup();
+              dstep(nd - 1, later, checked, nic, nd + 1, false);
+            }
           }
         };
         // at most 64 real rows in this wave's 128: fragments 2 and 3 are padding
@@ -1050,12 +1089,14 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
           kloop(std::integral_constant<int, 2>{});
         else
           kloop(std::integral_constant<int, 4>{});
-        vm_wait<0>();
+        // with the prefetch (no staged epilogue) the next item's slice 1
+        // stays in flight through the epilogue
+        if (!xp || STAGED) vm_wait<0>();
         wait_frags(f0a, f0b);
       }
       __builtin_amdgcn_s_barrier();
       if constexpr (!GATHER) {
-        next_setup();
+        if (!xp) next_setup();
       } else if constexpr (FP8) {
         // FP8 fragments leave no registers for setup inside the K-loop: the
         // next item is set up here and its index loads drained before any
@@ -1063,23 +1104,33 @@ __global__ __launch_bounds__(NTHR8, 1) void grouped_gemm_dma_kernel(
         next_setup();
         vm_wait<0>();
       }
-      if (has_next) issue_next(cur, std::true_type{});
+      if (has_next) issue_next(cur, std::true_type{}, xp);
       epilogue(done);
       // staged down: every wave has read its tile before slice 1 enters stage 1
       if constexpr (STAGED) __builtin_amdgcn_s_barrier();
     } else {
-      for (int d = 0; d < dlast; ++d) pass_step(d);
-      if constexpr (GATHER) {
+      if constexpr (xp) {
+        for (int d = 0; d < nd - 2; ++d) pass_step(d + 2, false);
         next_setup();
-        pass_step(nd - 1);
+        pass_step(has_next ? 0 : nd, has_next);
+        pass_step(has_next && !STAGED ? 1 : nd + 1, false);
+        if (STAGED) vm_wait<0>();
+      } else {
+        for (int d = 0; d < dlast; ++d) pass_step(d + 2, false);
+        if constexpr (GATHER) {
+          next_setup();
+          pass_step(nd + 1, false);
+        }
+        vm_wait<0>();
       }
-      vm_wait<0>();
       __builtin_amdgcn_s_barrier();
-      if constexpr (!GATHER) next_setup();
-      if (has_next) issue_next(cur, std::true_type{});
+      if constexpr (!GATHER) {
+        if (!xp) next_setup();
+      }
+      if (has_next) issue_next(cur, std::true_type{}, xp);
       if constexpr (STAGED) __builtin_amdgcn_s_barrier();  // the computing waves' second one
     }
-    if (has_next) issue_next(cur, std::false_type{});
+    if (has_next) issue_next(cur, std::false_type{}, xp);
     item = nxt;
   }
   vm_wait<0>();
@@ -1102,6 +1153,10 @@ int gemm_grid(int max_rows, int S, int N, int BN, int max_blocks) {
 
 // The direct-to-LDS kernel needs whole 64-wide K-slices, at least two.
 bool dma_ok(int Kd) { return Kd % WBK == 0 && Kd >= 2 * WBK; }
+// The cross-item prefetch: an even number of K-slices (the next item's first
+// two slices land in the stages the current item's last two would use), at
+// least four.
+bool xp_ok(int Kd) { return (Kd / WBK) % 2 == 0 && Kd / WBK >= 4; }
 
 }  // namespace
 
@@ -1117,14 +1172,21 @@ moe_status_t launch_gemm_bf16(moe_gemm_op_t op, const void* a, const int32_t* of
   const uint4* w4 = static_cast<const uint4*>(w);
   uint16_t* c16 = static_cast<uint16_t*>(c);
   const bool dma = dma_ok(Kd);
+  const bool xp = dma && xp_ok(Kd);
   if (op == MOE_GEMM_GATE_UP_SWIGLU) {
-    if (dma)
+    if (xp)
+      grouped_gemm_dma_kernel<0, false, false, true><<<G, NTHR8, 0, stream>>>(
+          a4, offsets, S, w4, N, Kd, c16, nullptr, 1, 0, 1.0f, nullptr, 1.0f);
+    else if (dma)
       grouped_gemm_dma_kernel<0, false, false><<<G, NTHR8, 0, stream>>>(
           a4, offsets, S, w4, N, Kd, c16, nullptr, 1, 0, 1.0f, nullptr, 1.0f);
     else
       grouped_gemm_bf16_kernel<0><<<G, NTHR, 0, stream>>>(a4, offsets, S, w4, N, Kd, c16);
   } else {
-    if (dma)
+    if (xp)
+      grouped_gemm_dma_kernel<1, false, false, true><<<G, NTHR8, 0, stream>>>(
+          a4, offsets, S, w4, N, Kd, c16, nullptr, 1, 0, 1.0f, nullptr, 1.0f);
+    else if (dma)
       grouped_gemm_dma_kernel<1, false, false><<<G, NTHR8, 0, stream>>>(
           a4, offsets, S, w4, N, Kd, c16, nullptr, 1, 0, 1.0f, nullptr, 1.0f);
     else
@@ -1146,9 +1208,14 @@ moe_status_t launch_gemm_bf16_gate_up_gathered(const void* x, int T, int K,
   if (!gemm_bf16_gather_ok(T, H)) return MOE_ERR_UNSUPPORTED;
   if (max_rows == 0) return MOE_OK;
   const int G = gemm_grid(max_rows, S, I, BROWS / 2, max_blocks);
-  grouped_gemm_dma_kernel<0, true, false><<<G, NTHR8, 0, stream>>>(
-      static_cast<const uint4*>(x), offsets, S, static_cast<const uint4*>(w), I, H, c,
-      sorted_pairs, K, T, 1.0f, nullptr, 1.0f);
+  if (xp_ok(H))
+    grouped_gemm_dma_kernel<0, true, false, true><<<G, NTHR8, 0, stream>>>(
+        static_cast<const uint4*>(x), offsets, S, static_cast<const uint4*>(w), I, H, c,
+        sorted_pairs, K, T, 1.0f, nullptr, 1.0f);
+  else
+    grouped_gemm_dma_kernel<0, true, false><<<G, NTHR8, 0, stream>>>(
+        static_cast<const uint4*>(x), offsets, S, static_cast<const uint4*>(w), I, H, c,
+        sorted_pairs, K, T, 1.0f, nullptr, 1.0f);
   return launch_status();
 }
 
