@@ -61,23 +61,33 @@
 extern "C" {
 #endif
 
+/* The *_ENUM_MIN_ / *_ENUM_MAX_ entries of the enums below are not values to
+ * pass or expect: they make every int a valid value of the enum type, so an
+ * out-of-range argument from a C caller is rejected with a status code
+ * instead of being undefined behaviour in the C++ implementation. */
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1, /* null pointer, negative size, K > E, E % ep_size != 0, ... */
   MOE_ERR_UNSUPPORTED = 2, /* dtype or shape outside what the kernels are built for */
   MOE_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than required */
-  MOE_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+  MOE_ERR_HIP = 4,         /* a HIP launch or runtime call failed */
+  MOE_STATUS_ENUM_MIN_ = -0x7fffffff - 1, /* see below: not status codes */
+  MOE_STATUS_ENUM_MAX_ = 0x7fffffff
 } moe_status_t;
 
 typedef enum {
   MOE_DTYPE_F32 = 0,
   MOE_DTYPE_BF16 = 1,
-  MOE_DTYPE_FP8_E4M3 = 2 /* OCP FP8 E4M3 codes (moe_quantize_fp8, moe_grouped_gemm_fp8) */
+  MOE_DTYPE_FP8_E4M3 = 2, /* OCP FP8 E4M3 codes (moe_quantize_fp8, moe_grouped_gemm_fp8) */
+  MOE_DTYPE_ENUM_MIN_ = -0x7fffffff - 1,
+  MOE_DTYPE_ENUM_MAX_ = 0x7fffffff
 } moe_dtype_t;
 
 typedef enum {
   MOE_GEMM_GATE_UP_SWIGLU = 0, /* c[r, j] = silu(a[r] . Wg[s, j]) * (a[r] . Wu[s, j]) */
-  MOE_GEMM_DOWN = 1            /* c[r, j] = a[r] . Wd[s, j] */
+  MOE_GEMM_DOWN = 1,           /* c[r, j] = a[r] . Wd[s, j] */
+  MOE_GEMM_OP_ENUM_MIN_ = -0x7fffffff - 1,
+  MOE_GEMM_OP_ENUM_MAX_ = 0x7fffffff
 } moe_gemm_op_t;
 
 /* Compiled limits. */

@@ -28,7 +28,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_FILE = os.path.join(_HERE, "libmoe_hip.so")
+# MOE_HIP_LIBRARY selects another build of the same library (the tests use it
+# for a host-sanitized build); it must exist like the default one.
+_LIB_FILE = os.environ.get("MOE_HIP_LIBRARY") or os.path.join(_HERE, "libmoe_hip.so")
 
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1

@@ -93,6 +93,32 @@ def _run(cmd, verbose, check_src=None):
         print(out, flush=True)
 
 
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the
+# validation and planning code (each flag applies to the host compilation
+# only; GPU code is not instrumented). Used by a CPU test, never shipped.
+SANITIZE_FLAGS = ["-g", "-fno-omit-frame-pointer",
+                  "-Xarch_host", "-fsanitize=address",
+                  "-Xarch_host", "-fsanitize=undefined"]
+
+
+def build_sanitized(out_dir: str, verbose: bool = False) -> str:
+    """Builds out_dir/libmoe_hip.so with host-side ASan and UBSan."""
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    os.makedirs(out_dir, exist_ok=True)
+    cc = hipcc()
+    objs = [os.path.join(out_dir, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    with _fut.ThreadPoolExecutor(min(len(srcs), os.cpu_count() or 1, 16)) as ex:
+        futs = [ex.submit(_run, [cc, *COMPILE_FLAGS, *SANITIZE_FLAGS, "-c", s, "-o", o], verbose)
+                for s, o in zip(srcs, objs)]
+        for f in futs:
+            f.result()
+    lib = os.path.join(out_dir, "libmoe_hip.so")
+    _run([cc, "-shared", f"--offload-arch={ARCH}", "-shared-libsan",
+          "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+          "-o", lib, *objs], verbose)
+    return lib
+
+
 def build(verbose: bool = False, jobs: int = 0) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not srcs:

@@ -224,6 +224,7 @@ const char* moe_status_str(moe_status_t status) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: dtype or shape not supported";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP launch or runtime error";
+    default: break;
   }
   return "unknown moe_status_t";
 }
