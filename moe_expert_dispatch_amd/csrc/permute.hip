@@ -6,8 +6,8 @@
 // experts, and the ragged gather that drops non-local pairs before compute.
 //
 // The result is a pure function of (slot, mask): within a slot, pairs keep
-// ascending pair index. Chunks are runs of whole tokens. Two launches, both
-// deterministic:
+// ascending pair index. Chunks are runs of whole tokens. Two index launches
+// and the row gather, all deterministic:
 //   1. count   one block per chunk: LDS histogram over slots, written
 //              slot-major: hist[s * nchunks + c].
 //   2. rank    one block per chunk. The block derives its own base rows from
@@ -16,12 +16,12 @@
 //              also writes offsets), so no separate scan launch sits between
 //              the two. Batches of 64 pairs are then ranked with a ballot
 //              per slot and per-batch counts scanned in LDS, so the order
-//              inside a chunk is the pair order. With the row gather, the
-//              block keeps its pairs' rows in LDS and copies each of its
-//              tokens' hidden row once from x to the rows its included
-//              pairs occupy (16-byte vectors, one wave per token).
-// A chunk too long for its rows to fit in LDS runs the gather as a third,
-// token-major launch instead.
+//              inside a chunk is the pair order.
+//   3. gather  token-major, one block per token: the token's row is read
+//              once and written to the K rows its included pairs occupy
+//              (16-byte vectors). (Folded into the ranking launch, with one
+//              block per chunk, it had too few blocks on small layers and
+//              was no faster on the largest.)
 #include <mutex>
 
 #include "common.h"
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
 constexpr int kRankThreads = 512;  // 8 waves: one batch of 64 pairs each per sub-chunk
 constexpr int kRankWaves = kRankThreads / kWave;
 static_assert(kBatches == kRankWaves, "one batch per wave");
-constexpr int kBaseRows = 8;  // histogram rows a wave sums at a time ...
+constexpr int kBaseRows = 16;  // histogram rows a wave sums at a time ...
 constexpr int kBaseCols = 4;  // ... and 64-entry column blocks of each, all loads in flight
 
 // Base rows of chunk c, from the per-chunk histograms hist[s * nchunks + j]
@@ -161,15 +161,14 @@ __device__ __forceinline__ void chunk_bases(const int32_t* __restrict__ hist, in
 // = pair order); per-batch slot counts, scanned over the batches, give each
 // batch's base row, so the order inside a slot is the pair order.
 // seg_cap > 0: slot s's rows start at s * seg_cap instead of offsets[s]
-// (fixed-capacity blocks, one per slot). rows_lds non-null: the rows of the
-// chunk's pairs are also kept there (index p - c * chunk).
+// (fixed-capacity blocks, one per slot).
 __device__ __forceinline__ void rank_chunk(int c, const int32_t* __restrict__ slot,
                                            const uint8_t* __restrict__ mask, int P, int S,
                                            int chunk, int nchunks,
                                            const int32_t* __restrict__ hist,
                                            int32_t* __restrict__ offsets, int seg_cap,
                                            int32_t* __restrict__ sorted_pairs,
-                                           int32_t* __restrict__ pair_row, int32_t* rows_lds) {
+                                           int32_t* __restrict__ pair_row) {
   extern __shared__ int32_t lds[];
   int32_t* running = lds;            // [S] next free row per slot
   int32_t* tot = lds + S;            // [S] slot totals (base computation)
@@ -178,16 +177,21 @@ __device__ __forceinline__ void rank_chunk(int c, const int32_t* __restrict__ sl
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
-  chunk_bases(hist, S, nchunks, c, seg_cap, running, tot, wsum, offsets);
   const int p0 = c * chunk;
   const int p1 = min(p0 + chunk, P);
+  // the first sub-chunk's pairs are loaded before the bases are summed, so
+  // the two memory round trips overlap
+  int s_first = -1;
+  const bool inc_first =
+      p0 + wave * kWave + lane < p1 && included(slot, mask, p0 + wave * kWave + lane, P, S, &s_first);
+  chunk_bases(hist, S, nchunks, c, seg_cap, running, tot, wsum, offsets);
   for (int q0 = p0; q0 < p1; q0 += kSub) {
     for (int i = tid; i < kBatches * S; i += kRankThreads) bcount[i] = 0;
     __syncthreads();
     const int b = wave;  // this wave's batch
     const int p = q0 + b * kWave + lane;
-    int s = -1;
-    const bool inc = p < p1 && included(slot, mask, p, P, S, &s);
+    int s = s_first;
+    const bool inc = q0 == p0 ? inc_first : p < p1 && included(slot, mask, p, P, S, &s);
     int rank = 0;
     uint64_t active = __ballot(inc);
     while (active) {
@@ -213,7 +217,6 @@ __device__ __forceinline__ void rank_chunk(int c, const int32_t* __restrict__ sl
       const int row = inc ? bcount[b * S + s] + rank : -1;
       pair_row[p] = row;
       if (row >= 0) sorted_pairs[row] = p;
-      if (rows_lds) rows_lds[p - p0] = row;
     }
     __syncthreads();
   }
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(
     int nchunks, const int32_t* __restrict__ hist, int32_t* __restrict__ offsets, int seg_cap,
     int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_row) {
   rank_chunk(blockIdx.x, slot, mask, P, S, chunk, nchunks, hist, offsets, seg_cap, sorted_pairs,
-             pair_row, nullptr);
+             pair_row);
 }
 
 // The ranking with a quantization riding along: blocks [0, rblocks) rank
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_quant_kernel(
     FusedQuant fq) {
   if ((int)blockIdx.x < rblocks)
     rank_chunk(blockIdx.x, slot, mask, P, S, chunk, nchunks, hist, offsets, seg_cap,
-               sorted_pairs, pair_row, nullptr);
+               sorted_pairs, pair_row);
   else
     quantize16(fq.x, fq.n, fq.inv, fq.q,
                (int64_t)(blockIdx.x - (unsigned)rblocks) * blockDim.x + threadIdx.x);
@@ -347,83 +350,6 @@ __global__ __launch_bounds__(256) void gather_scaled_kernel(const uint4* __restr
   gather_rows<true, ET>(x + (size_t)t * nvec, nvec, K, rows, ws, x_perm);
 }
 
-// Ranking of chunk c followed by the row gather of its tokens, one wave per
-// token (tokens t0 + w, t0 + w + 8, ...): the token's row is loaded
-// (kWaveVec 16-byte vectors per lane at a time, all in flight) and stored to
-// the rows its included pairs occupy, which the ranking left in LDS.
-constexpr int kWaveVec = 8;
-constexpr size_t kMaxRankLds = 65536;  // bytes of dynamic LDS a ranking block may use
-
-template <bool SCALED, typename ET>
-__global__ __launch_bounds__(kRankThreads) void rank_gather_kernel(
-    const int32_t* __restrict__ slot, const uint8_t* __restrict__ mask, int P, int S, int chunk,
-    int nchunks, const int32_t* __restrict__ hist, int32_t* __restrict__ offsets, int seg_cap,
-    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_row,
-    const uint4* __restrict__ x, int nvec, int K, const float* __restrict__ pair_w,
-    uint4* __restrict__ x_perm) {
-  extern __shared__ int32_t lds[];
-  const int c = blockIdx.x;
-  int32_t* rows_lds = lds + (2 + kBatches) * S + kRankWaves;
-  rank_chunk(c, slot, mask, P, S, chunk, nchunks, hist, offsets, seg_cap, sorted_pairs,
-             pair_row, rows_lds);  // ends with a barrier: rows_lds is complete
-  const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
-  const int tpc = chunk / K;
-  const int t0 = c * tpc;
-  const int t1 = min(t0 + tpc, P / K);
-  const uint32_t row_bytes = (uint32_t)nvec * 16u;
-  auto load_row = [&](int t, int v0, int32x4_t* val) {
-    const __amdgpu_buffer_rsrc_t sr = row_rsrc(x + (size_t)t * nvec, row_bytes);
-#pragma unroll
-    for (int u = 0; u < kWaveVec; ++u) {
-      const int v = v0 + u * kWave;
-      val[u] = __builtin_amdgcn_raw_buffer_load_b128(sr, v < nvec ? (uint32_t)v * 16u : row_bytes,
-                                                     0, 0);
-    }
-  };
-  auto store_rows = [&](int t, int v0, const int32x4_t* val) {
-    for (int k = 0; k < K; ++k) {
-      const int r = rows_lds[(t - t0) * K + k];
-      if (r < 0) continue;  // wave-uniform
-      float wk = 1.0f;
-      if constexpr (SCALED) wk = pair_w[(size_t)t * K + k];
-      const __amdgpu_buffer_rsrc_t dr = row_rsrc(x_perm + (size_t)r * nvec, row_bytes);
-#pragma unroll
-      for (int u = 0; u < kWaveVec; ++u) {
-        const int v = v0 + u * kWave;
-        int32x4_t o = val[u];
-        if constexpr (SCALED) o = scale_row(o, wk, (const ET*)nullptr);
-        __builtin_amdgcn_raw_buffer_store_b128(o, dr, v < nvec ? (uint32_t)v * 16u : row_bytes,
-                                               0, kNonTemporal);
-      }
-    }
-  };
-  if (nvec <= kWaveVec * kWave) {
-    // a row is one load step: the wave's next token is loaded while the
-    // current one is stored
-    int32x4_t cur[kWaveVec], nxt[kWaveVec];
-    int t = t0 + wave;
-    if (t < t1) load_row(t, lane, cur);
-    for (; t < t1; t += kRankWaves) {
-      const bool more = t + kRankWaves < t1;  // wave-uniform
-      if (more) load_row(t + kRankWaves, lane, nxt);
-      store_rows(t, lane, cur);
-      if (more) {
-#pragma unroll
-        for (int u = 0; u < kWaveVec; ++u) cur[u] = nxt[u];
-      }
-    }
-  } else {
-    for (int t = t0 + wave; t < t1; t += kRankWaves) {
-      for (int v0 = lane; v0 < nvec; v0 += kWaveVec * kWave) {
-        int32x4_t val[kWaveVec];
-        load_row(t, v0, val);
-        store_rows(t, v0, val);
-      }
-    }
-  }
-}
-
 }  // namespace
 
 PermutePlan permute_plan(int T, int K, int S) {
@@ -479,37 +405,21 @@ moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
   // at least one ranking block: chunk 0 writes offsets (all zero when empty)
   const int rblocks = pl.nchunks > 0 ? pl.nchunks : 1;
   const size_t lds_rank = ((size_t)(2 + kBatches) * S + kRankWaves) * sizeof(int32_t);
-  const size_t lds_fused = lds_rank + (size_t)pl.chunk * sizeof(int32_t);
-  const int nvec = H * elem_bytes / 16;
-  const uint4* x4 = static_cast<const uint4*>(x);
-  uint4* xp4 = static_cast<uint4*>(x_perm);
-  const bool gather = x_perm != nullptr && T > 0;
-  const bool fused = gather && lds_fused <= kMaxRankLds;
   const int64_t qblocks = (quant != nullptr && quant->n > 0)
                               ? ((quant->n + 15) / 16 + kRankThreads - 1) / kRankThreads
                               : 0;
-  if (qblocks > 0) {
+  if (qblocks > 0)
     rank_quant_kernel<<<(unsigned)(rblocks + qblocks), kRankThreads, lds_rank, stream>>>(
         slot, mask, pl.P, S, pl.chunk, pl.nchunks, rblocks, hist, offsets, seg_cap,
         sorted_pairs, pair_row, *quant);
-  } else if (fused && pair_w == nullptr) {
-    rank_gather_kernel<false, uint16_t><<<rblocks, kRankThreads, lds_fused, stream>>>(
-        slot, mask, pl.P, S, pl.chunk, pl.nchunks, hist, offsets, seg_cap, sorted_pairs,
-        pair_row, x4, nvec, K, nullptr, xp4);
-  } else if (fused && elem_bytes == 2) {
-    rank_gather_kernel<true, uint16_t><<<rblocks, kRankThreads, lds_fused, stream>>>(
-        slot, mask, pl.P, S, pl.chunk, pl.nchunks, hist, offsets, seg_cap, sorted_pairs,
-        pair_row, x4, nvec, K, pair_w, xp4);
-  } else if (fused) {
-    rank_gather_kernel<true, float><<<rblocks, kRankThreads, lds_fused, stream>>>(
-        slot, mask, pl.P, S, pl.chunk, pl.nchunks, hist, offsets, seg_cap, sorted_pairs,
-        pair_row, x4, nvec, K, pair_w, xp4);
-  } else {
+  else
     rank_kernel<<<rblocks, kRankThreads, lds_rank, stream>>>(slot, mask, pl.P, S, pl.chunk,
                                                              pl.nchunks, hist, offsets, seg_cap,
                                                              sorted_pairs, pair_row);
-  }
-  if (gather && !fused) {  // chunks too long for their rows to stay in LDS
+  if (x_perm != nullptr && T > 0) {
+    const int nvec = H * elem_bytes / 16;
+    const uint4* x4 = static_cast<const uint4*>(x);
+    uint4* xp4 = static_cast<uint4*>(x_perm);
     if (pair_w == nullptr)
       gather_kernel<<<T, 256, 0, stream>>>(x4, T, nvec, K, pair_row, xp4);
     else if (elem_bytes == 2)
