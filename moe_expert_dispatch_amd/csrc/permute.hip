@@ -14,9 +14,9 @@
 //              all histograms (slot totals, their exclusive scan over slots,
 //              plus the counts of the earlier chunks of each slot; chunk 0
 //              also writes offsets), so no separate scan launch sits between
-//              the two. Batches of 64 pairs are then ranked with a ballot
-//              per slot and per-batch counts scanned in LDS, so the order
-//              inside a chunk is the pair order.
+//              the two. Batches of 64 pairs are then ranked with one ballot
+//              per bit of the slot id and per-batch counts scanned in LDS,
+//              so the order inside a chunk is the pair order.
 //   3. gather  token-major, one block per token: the token's row is read
 //              once and written to the K rows its included pairs occupy
 //              (16-byte vectors). (Folded into the ranking launch, with one
@@ -157,9 +157,10 @@ __device__ __forceinline__ void chunk_bases(const int32_t* __restrict__ hist, in
 
 // Ranking and scatter of chunk c (one block of kRankThreads). The chunk is
 // walked in sub-chunks of 512 pairs = 8 batches of 64, one per wave. Inside a
-// batch the lanes holding the same slot are ranked with a ballot (lane order
-// = pair order); per-batch slot counts, scanned over the batches, give each
-// batch's base row, so the order inside a slot is the pair order.
+// batch a lane's rank is the number of lower lanes holding the same slot
+// (lane order = pair order), found from one ballot per bit of the slot id;
+// per-batch slot counts, scanned over the batches, give each batch's base
+// row, so the order inside a slot is the pair order.
 // seg_cap > 0: slot s's rows start at s * seg_cap instead of offsets[s]
 // (fixed-capacity blocks, one per slot).
 __device__ __forceinline__ void rank_chunk(int c, const int32_t* __restrict__ slot,
@@ -179,6 +180,7 @@ __device__ __forceinline__ void rank_chunk(int c, const int32_t* __restrict__ sl
   const int wave = tid / kWave;
   const int p0 = c * chunk;
   const int p1 = min(p0 + chunk, P);
+  const int sbits = S > 1 ? 32 - __clz(S - 1) : 0;  // bits of the largest slot id
   // the first sub-chunk's pairs are loaded before the bases are summed, so
   // the two memory round trips overlap
   int s_first = -1;
@@ -192,16 +194,18 @@ __device__ __forceinline__ void rank_chunk(int c, const int32_t* __restrict__ sl
     const int p = q0 + b * kWave + lane;
     int s = s_first;
     const bool inc = q0 == p0 ? inc_first : p < p1 && included(slot, mask, p, P, S, &s);
-    int rank = 0;
-    uint64_t active = __ballot(inc);
-    while (active) {
-      const int leader = __ffsll((unsigned long long)active) - 1;
-      const int ls = __shfl(s, leader, kWave);
-      const uint64_t same = __ballot(inc && s == ls);
-      if (inc && s == ls) rank = __popcll(same & lanemask_lt());
-      if (lane == leader) bcount[b * S + ls] = __popcll(same);
-      active &= ~same;
+    // Lanes holding the same slot: the included lanes whose slot id agrees
+    // with this lane's in every bit, one ballot per bit of S - 1 (no loop
+    // over the batch's distinct slots, no cross-lane reads).
+    uint64_t same = __ballot(inc);
+    for (int bit = 0; bit < sbits; ++bit) {
+      const bool on = (s >> bit) & 1;
+      const uint64_t ones = __ballot(inc && on);
+      same &= on ? ones : ~ones;
     }
+    const uint64_t below = same & lanemask_lt();
+    const int rank = __popcll(below);
+    if (inc && below == 0) bcount[b * S + s] = __popcll(same);  // first lane of its slot
     __syncthreads();
     for (int i = tid; i < S; i += kRankThreads) {
       int run = running[i];
