@@ -121,9 +121,11 @@ def run_a2a(args):
     t_g = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
     sent = int((state["d"][1] >= 0).sum().item())  # (token, rank) messages
     eb = 2
-    # dispatch: read each token row once, write one row per message, plus the
-    # routing copied with it and the index arrays
-    d_bytes = T * cfg.H * eb + sent * cfg.H * eb + R * T * cfg.K * 8 + T * R * 9 + T * cfg.K * 4
+    # dispatch: read each token row and its routing once, write one row per
+    # message, the routing of every send row (ids, weights, token) and the
+    # token positions
+    d_bytes = (T * cfg.H * eb + sent * cfg.H * eb + T * cfg.K * 8 + R * T * (cfg.K * 8 + 4)
+               + T * R * 4)
     g_bytes = sent * cfg.H * 4 + T * cfg.H * eb + T * R * 4
     step = t_d + t_x + t_g
     res = {"metric": "all-to-all expert-parallel layer tokens/sec (dispatch, per-rank experts, "

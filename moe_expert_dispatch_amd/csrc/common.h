@@ -306,15 +306,14 @@ constexpr int kPermuteScratchInts = 65536;
 // Device address of that array on the current device, looked up on the
 // first call per device (hipGetSymbolAddress) and kept for later calls.
 moe_status_t permute_scratch(int32_t** out);
-// seg_cap > 0 places slot s's rows in the fixed block [s * seg_cap,
-// (s + 1) * seg_cap) (the caller guarantees every slot fits). pair_w non-null:
-// the row of pair p is pair_w[p] * x[p / K] (f32 product, rounded once).
-// quant non-null: its quantization runs as extra blocks of the scatter launch.
+// pair_w non-null: the row of pair p is pair_w[p] * x[p / K] (f32 product,
+// rounded once). quant non-null: its quantization runs as extra blocks of the
+// ranking launch.
 moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
                             const int32_t* slot, const uint8_t* mask, int S, int32_t* offsets,
                             int32_t* sorted_pairs, int32_t* pair_row, void* x_perm, void* ws,
-                            hipStream_t stream, int seg_cap = 0,
-                            const float* pair_w = nullptr, const FusedQuant* quant = nullptr);
+                            hipStream_t stream, const float* pair_w = nullptr,
+                            const FusedQuant* quant = nullptr);
 
 // max_blocks > 0 caps the persistent GEMM grid (default: one block per
 // compute unit); the results do not depend on the grid.
@@ -357,7 +356,7 @@ moe_status_t launch_quantize_fp8(const void* x, bool x_bf16, int64_t n, float sc
 
 // All-to-all dispatch workspace (carved in this order, 256-byte aligned).
 struct A2aLayout {
-  size_t pslot, pmask, psorted, perm_ws, total;
+  size_t bits, hist, total;  // per-token rank masks, per-chunk rank counts
 };
 A2aLayout a2a_layout(int T, int R, int cap);
 moe_status_t launch_a2a_dispatch(const void* x, int elem_bytes, int T, int H, int K,

@@ -302,7 +302,7 @@ moe_status_t moe_permute_scaled(const void* x, moe_dtype_t dt, int T, int H, int
   if (st != MOE_OK) return st;
   if (T > 0 && (!pair_w || !x_perm)) return MOE_ERR_INVALID_ARG;
   return launch_permute(x, dtype_bytes(dt), T, H, K, slot, mask, S, offsets, sorted_pairs,
-                        pair_row, x_perm, ws, stream, 0, pair_w);
+                        pair_row, x_perm, ws, stream, pair_w);
 }
 
 moe_status_t moe_grouped_gemm(moe_gemm_op_t op, moe_dtype_t dt, const void* a,
@@ -415,7 +415,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_forward_args_t* args
                       1.0f / cfg->a1_scale, xq};
   MOE_TRY(launch_permute(args->x, fp8 ? 2 : dtype_bytes(cfg->dtype), T, H, K, slot, mask, S,
                          offsets, sorted_pairs, pair_row, fused_gather ? nullptr : x_perm,
-                         perm_ws, stream, 0, on_input ? w_masked : nullptr,
+                         perm_ws, stream, on_input ? w_masked : nullptr,
                          fp8 ? &fq : nullptr));
   MOE_TRY(mark(MOE_EV_PERMUTED));
   if (fp8)

@@ -25,6 +25,7 @@
 #include <mutex>
 
 #include "common.h"
+#include "row_gather.h"
 
 // Histogram memory of moe_permute_noalloc: one static array per device
 // (each GPU the library runs on holds its own copy until the process ends).
@@ -73,12 +74,12 @@ constexpr int kBaseCols = 4;  // ... and 64-entry column blocks of each, all loa
 
 // Base rows of chunk c, from the per-chunk histograms hist[s * nchunks + j]
 // (counts): tot[s] = sum over j of hist[s][j], pre[s] = sum over j < c;
-// the slot's first row is the exclusive scan of tot over slots (or s *
-// seg_cap for fixed-capacity blocks). running[s] = first row + pre[s].
+// the slot's first row is the exclusive scan of tot over slots.
+// running[s] = first row + pre[s].
 // Chunk 0 writes offsets[s] (the scan) and offsets[S] (all included pairs).
 // tot and wsum are LDS scratch ([S], [kRankWaves]).
 __device__ __forceinline__ void chunk_bases(const int32_t* __restrict__ hist, int S, int nchunks,
-                                            int c, int seg_cap, int32_t* running, int32_t* tot,
+                                            int c, int32_t* running, int32_t* tot,
                                             int32_t* wsum, int32_t* __restrict__ offsets) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -142,13 +143,11 @@ __device__ __forceinline__ void chunk_bases(const int32_t* __restrict__ hist, in
   }
   const int first = before + incl - (a + b);  // first row of slot 2t
   if (2 * tid < S) {
-    const int r0 = seg_cap > 0 ? 2 * tid * seg_cap : first;
-    running[2 * tid] += r0;
+    running[2 * tid] += first;
     if (c == 0) offsets[2 * tid] = first;
   }
   if (2 * tid + 1 < S) {
-    const int r1 = seg_cap > 0 ? (2 * tid + 1) * seg_cap : first + a;
-    running[2 * tid + 1] += r1;
+    running[2 * tid + 1] += first + a;
     if (c == 0) offsets[2 * tid + 1] = first + a;
   }
   if (c == 0 && tid == 0) offsets[S] = total;
@@ -161,13 +160,11 @@ __device__ __forceinline__ void chunk_bases(const int32_t* __restrict__ hist, in
 // (lane order = pair order), found from one ballot per bit of the slot id;
 // per-batch slot counts, scanned over the batches, give each batch's base
 // row, so the order inside a slot is the pair order.
-// seg_cap > 0: slot s's rows start at s * seg_cap instead of offsets[s]
-// (fixed-capacity blocks, one per slot).
 __device__ __forceinline__ void rank_chunk(int c, const int32_t* __restrict__ slot,
                                            const uint8_t* __restrict__ mask, int P, int S,
                                            int chunk, int nchunks,
                                            const int32_t* __restrict__ hist,
-                                           int32_t* __restrict__ offsets, int seg_cap,
+                                           int32_t* __restrict__ offsets,
                                            int32_t* __restrict__ sorted_pairs,
                                            int32_t* __restrict__ pair_row) {
   extern __shared__ int32_t lds[];
@@ -186,7 +183,7 @@ __device__ __forceinline__ void rank_chunk(int c, const int32_t* __restrict__ sl
   int s_first = -1;
   const bool inc_first =
       p0 + wave * kWave + lane < p1 && included(slot, mask, p0 + wave * kWave + lane, P, S, &s_first);
-  chunk_bases(hist, S, nchunks, c, seg_cap, running, tot, wsum, offsets);
+  chunk_bases(hist, S, nchunks, c, running, tot, wsum, offsets);
   for (int q0 = p0; q0 < p1; q0 += kSub) {
     for (int i = tid; i < kBatches * S; i += kRankThreads) bcount[i] = 0;
     __syncthreads();
@@ -228,9 +225,9 @@ __device__ __forceinline__ void rank_chunk(int c, const int32_t* __restrict__ sl
 
 __global__ __launch_bounds__(kRankThreads) void rank_kernel(
     const int32_t* __restrict__ slot, const uint8_t* __restrict__ mask, int P, int S, int chunk,
-    int nchunks, const int32_t* __restrict__ hist, int32_t* __restrict__ offsets, int seg_cap,
+    int nchunks, const int32_t* __restrict__ hist, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_row) {
-  rank_chunk(blockIdx.x, slot, mask, P, S, chunk, nchunks, hist, offsets, seg_cap, sorted_pairs,
+  rank_chunk(blockIdx.x, slot, mask, P, S, chunk, nchunks, hist, offsets, sorted_pairs,
              pair_row);
 }
 
@@ -242,40 +239,15 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(
 __global__ __launch_bounds__(kRankThreads) void rank_quant_kernel(
     const int32_t* __restrict__ slot, const uint8_t* __restrict__ mask, int P, int S, int chunk,
     int nchunks, int rblocks, const int32_t* __restrict__ hist, int32_t* __restrict__ offsets,
-    int seg_cap, int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_row,
+    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_row,
     FusedQuant fq) {
   if ((int)blockIdx.x < rblocks)
-    rank_chunk(blockIdx.x, slot, mask, P, S, chunk, nchunks, hist, offsets, seg_cap,
+    rank_chunk(blockIdx.x, slot, mask, P, S, chunk, nchunks, hist, offsets,
                sorted_pairs, pair_row);
   else
     quantize16(fq.x, fq.n, fq.inv, fq.q,
                (int64_t)(blockIdx.x - (unsigned)rblocks) * blockDim.x + threadIdx.x);
 }
-
-typedef int int32x4_t __attribute__((ext_vector_type(4)));
-
-// Raw buffer resource over [base, base + bytes): an offset at or past the end
-// reads zeros and drops stores, so vector tails need no branch.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-// The permuted rows are written once and read by a later kernel, long after
-// they would have left the caches, so their stores carry the non-temporal
-// policy (bit 1 of the cache-policy operand, NT on gfx950). Measured on
-// 16384 tokens x 8 rows of 8 KB scattered in random order: 235 us with the
-// default policy, 209 us non-temporal (non-temporal loads of x as well: 252).
-constexpr int kNonTemporal = 2;
-constexpr int kGatherVec = 2;  // 16-byte vectors per thread loaded before the stores
-
-// One block per token: the token's row is loaded once (kGatherVec vectors
-// per thread, all in flight), then stored to each included pair's row.
-// scale_row (below) gives input-side routing its weighted rows.
-template <bool SCALED, typename ET>
-__device__ __forceinline__ void gather_rows(const uint4* __restrict__ x, int nvec, int K,
-                                            const int32_t* rows, const float* ws,
-                                            uint4* __restrict__ x_perm);
 
 __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x, int T,
                                                      int nvec, int K,
@@ -286,55 +258,6 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x
   if (threadIdx.x < K) rows[threadIdx.x] = pair_row[(size_t)t * K + threadIdx.x];
   __syncthreads();
   gather_rows<false, uint16_t>(x + (size_t)t * nvec, nvec, K, rows, nullptr, x_perm);
-}
-
-// Input-side routing: the row of pair (t, k) is x[t] scaled by the pair's
-// weight, w * x evaluated in f32 and rounded once to the element type.
-__device__ __forceinline__ int32x4_t scale_row(int32x4_t v, float s, const uint16_t*) {
-  int32x4_t o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t q = (uint32_t)v[i];
-    o[i] = (int)pack_bf16x2(bf16_to_f32(q & 0xffffu) * s, bf16_to_f32(q >> 16) * s);
-  }
-  return o;
-}
-
-__device__ __forceinline__ int32x4_t scale_row(int32x4_t v, float s, const float*) {
-  int32x4_t o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = __float_as_int(__int_as_float(v[i]) * s);
-  return o;
-}
-
-template <bool SCALED, typename ET>
-__device__ __forceinline__ void gather_rows(const uint4* __restrict__ src, int nvec, int K,
-                                            const int32_t* rows, const float* ws,
-                                            uint4* __restrict__ x_perm) {
-  const uint32_t row_bytes = (uint32_t)nvec * 16u;
-  const __amdgpu_buffer_rsrc_t sr = row_rsrc(src, row_bytes);
-  for (int v0 = threadIdx.x; v0 < nvec; v0 += kGatherVec * blockDim.x) {
-    int32x4_t val[kGatherVec];
-#pragma unroll
-    for (int u = 0; u < kGatherVec; ++u) {
-      const int v = v0 + u * blockDim.x;
-      val[u] = __builtin_amdgcn_raw_buffer_load_b128(sr, v < nvec ? (uint32_t)v * 16u : row_bytes,
-                                                     0, 0);
-    }
-    for (int k = 0; k < K; ++k) {
-      const int r = rows[k];
-      if (r < 0) continue;  // block-uniform
-      const __amdgpu_buffer_rsrc_t dr = row_rsrc(x_perm + (size_t)r * nvec, row_bytes);
-#pragma unroll
-      for (int u = 0; u < kGatherVec; ++u) {
-        const int v = v0 + u * blockDim.x;
-        int32x4_t o = val[u];
-        if constexpr (SCALED) o = scale_row(o, ws[k], (const ET*)nullptr);
-        __builtin_amdgcn_raw_buffer_store_b128(
-            o, dr, v < nvec ? (uint32_t)v * 16u : row_bytes, 0, kNonTemporal);
-      }
-    }
-  }
 }
 
 template <typename ET>
@@ -398,7 +321,7 @@ moe_status_t permute_scratch(int32_t** out) {
 moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
                             const int32_t* slot, const uint8_t* mask, int S, int32_t* offsets,
                             int32_t* sorted_pairs, int32_t* pair_row, void* x_perm, void* ws,
-                            hipStream_t stream, int seg_cap, const float* pair_w,
+                            hipStream_t stream, const float* pair_w,
                             const FusedQuant* quant) {
   const PermutePlan pl = permute_plan(T, K, S);
   int32_t* hist = static_cast<int32_t*>(ws);
@@ -414,11 +337,11 @@ moe_status_t launch_permute(const void* x, int elem_bytes, int T, int H, int K,
                               : 0;
   if (qblocks > 0)
     rank_quant_kernel<<<(unsigned)(rblocks + qblocks), kRankThreads, lds_rank, stream>>>(
-        slot, mask, pl.P, S, pl.chunk, pl.nchunks, rblocks, hist, offsets, seg_cap,
+        slot, mask, pl.P, S, pl.chunk, pl.nchunks, rblocks, hist, offsets,
         sorted_pairs, pair_row, *quant);
   else
     rank_kernel<<<rblocks, kRankThreads, lds_rank, stream>>>(slot, mask, pl.P, S, pl.chunk,
-                                                             pl.nchunks, hist, offsets, seg_cap,
+                                                             pl.nchunks, hist, offsets,
                                                              sorted_pairs, pair_row);
   if (x_perm != nullptr && T > 0) {
     const int nvec = H * elem_bytes / 16;

@@ -34,6 +34,8 @@ def _routing(T, E, K, seed, invalid=0.0):
     (300, 136, 16, 4, 4, 310, 0.1, torch.bfloat16),
     (129, 64, 12, 3, 3, 129, 0.0, torch.float32),
     (50, 64, 32, 8, 8, 50, 0.05, torch.bfloat16),
+    (600, 64, 64, 4, 32, 700, 0.05, torch.bfloat16),
+    (1000, 32, 24, 6, 6, 1024, 0.02, torch.float32),
     (40, 64, 6, 2, 1, 40, 0.0, torch.bfloat16),
     (0, 64, 8, 2, 2, 5, 0.0, torch.bfloat16),
     (8192, 2048, 256, 8, 4, 8192, 0.0, torch.bfloat16),
