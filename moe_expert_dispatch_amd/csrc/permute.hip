@@ -69,8 +69,13 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
 constexpr int kRankThreads = 512;  // 8 waves: one batch of 64 pairs each per sub-chunk
 constexpr int kRankWaves = kRankThreads / kWave;
 static_assert(kBatches == kRankWaves, "one batch per wave");
-constexpr int kBaseRows = 16;  // histogram rows a wave sums at a time ...
-constexpr int kBaseCols = 4;  // ... and 64-entry column blocks of each, all loads in flight
+// Histogram rows a wave sums at a time, and 64-entry column blocks of each:
+// all kBaseRows * kBaseCols loads in flight. Four rows keep the ranking at 49
+// registers, so it leaves room for the quantization blocks that share its
+// launch (sixteen rows: 157 registers, three waves per SIMD, and the FP8
+// permute stage 25-30% slower); the ranking alone is no slower for it.
+constexpr int kBaseRows = 4;
+constexpr int kBaseCols = 4;
 
 // Base rows of chunk c, from the per-chunk histograms hist[s * nchunks + j]
 // (counts): tot[s] = sum over j of hist[s][j], pre[s] = sum over j < c;
