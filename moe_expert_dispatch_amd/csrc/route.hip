@@ -129,11 +129,12 @@ __global__ __launch_bounds__(256) void route_lanes_kernel(const float* __restric
 }
 
 // G == 0: plain top-K over all experts; otherwise 1 <= TG <= G <= 64, E % G == 0.
-template <int EPL>
+// MAP: the slot map of each selected pair as well (as in the lane-group form).
+template <int EPL, bool MAP>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T,
                                                     int E, int K, int renorm, int G, int TG,
                                                     int32_t* __restrict__ ids,
-                                                    float* __restrict__ w) {
+                                                    float* __restrict__ w, MapOut mo) {
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (t >= T) return;  // wave-uniform
   const int lane = lane_id();
@@ -155,13 +156,18 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 
   if (G > 0) {
     const int Eg = E / G;
+    int grp[EPL];  // group of each of the lane's experts (-1: none)
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + kWave * j;
+      grp[j] = e < E ? e / Eg : -1;
+    }
     uint64_t gkey = 0;
     for (int g = 0; g < G; ++g) {
       uint32_t m = 0;
 #pragma unroll
       for (int j = 0; j < EPL; ++j) {
-        const int e = lane + kWave * j;
-        if (e < E && e / Eg == g) {
+        if (grp[j] == g) {
           const uint32_t o = (uint32_t)(key[j] >> 32);
           m = o > m ? o : m;
         }
@@ -177,10 +183,8 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
       if (lane == g) gkey = 0;
     }
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      const int e = lane + kWave * j;
-      if (e < E && !((keep >> (e / Eg)) & 1ull)) key[j] = 0;
-    }
+    for (int j = 0; j < EPL; ++j)
+      if (grp[j] >= 0 && !((keep >> grp[j]) & 1ull)) key[j] = 0;
   }
 
   // K rounds of wave max; lane k keeps the k-th selection.
@@ -197,7 +201,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
       if (lane + kWave * j == e) key[j] = 0;
     if (lane == k) {
       my_id = e;
-      my_logit = row[e];
+      my_logit = from_ordered((uint32_t)(best >> 32));
     }
   }
 
@@ -214,8 +218,12 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     p = p / s;
   }
   if (lane < K) {
-    ids[(size_t)t * K + lane] = my_id;
-    w[(size_t)t * K + lane] = p;
+    const int pi = t * K + lane;
+    ids[pi] = my_id;
+    w[pi] = p;
+    if constexpr (MAP)
+      map_pair(pi, t, my_id, p, mo.start, mo.E_local, mo.rep_off, mo.rep_slots, mo.S, mo.slot,
+               mo.w_masked, mo.mask);
   }
 }
 
@@ -244,6 +252,26 @@ void launch_lanes(const float* logits, int T, int E, int K, int renorm, int32_t*
     route_lanes_kernel<L, 8, MAP><<<grid, 256, 0, stream>>>(logits, T, E, K, renorm, ids, w, mo);
 }
 
+// One wave per token (group-limited routing, more than 256 experts, K > 32).
+template <bool MAP>
+void launch_waves(const float* logits, int T, int E, int K, int renorm, int G, int TG,
+                  int32_t* ids, float* w, const MapOut& mo, hipStream_t stream) {
+  const dim3 block(256);
+  const dim3 grid(ceil_div(T, 256 / kWave));
+  const int epl = ceil_div(E, kWave);
+  if (epl <= 1)
+    route_kernel<1, MAP><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, G, TG, ids, w, mo);
+  else if (epl <= 2)
+    route_kernel<2, MAP><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, G, TG, ids, w, mo);
+  else if (epl <= 4)
+    route_kernel<4, MAP><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, G, TG, ids, w, mo);
+  else if (epl <= 8)
+    route_kernel<8, MAP><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, G, TG, ids, w, mo);
+  else
+    route_kernel<16, MAP><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, G, TG, ids, w,
+                                                      mo);
+}
+
 template <bool MAP>
 void launch_lanes_any(int L, const float* logits, int T, int E, int K, int renorm, int32_t* ids,
                       float* w, const MapOut& mo, hipStream_t stream) {
@@ -264,14 +292,11 @@ moe_status_t launch_route_map(const float* logits, int T, int E, int K, int reno
                               hipStream_t stream) {
   if (T == 0) return MOE_OK;
   const int L = lanes_for(E, K, G);
-  if (L == 0) {
-    const moe_status_t st = launch_route(logits, T, E, K, renorm, G, TG, ids, w, stream);
-    if (st != MOE_OK) return st;
-    return launch_slot_map(ids, w, T, K, start, E_local, rep_off, rep_slots, S, slot, w_masked,
-                           mask, stream);
-  }
   const MapOut mo{start, E_local, S, rep_off, rep_slots, slot, w_masked, mask};
-  launch_lanes_any<true>(L, logits, T, E, K, renorm, ids, w, mo, stream);
+  if (L == 0)
+    launch_waves<true>(logits, T, E, K, renorm, G, TG, ids, w, mo, stream);
+  else
+    launch_lanes_any<true>(L, logits, T, E, K, renorm, ids, w, mo, stream);
   return launch_status();
 }
 
@@ -282,19 +307,7 @@ moe_status_t launch_route(const float* logits, int T, int E, int K, int renorm, 
     launch_lanes_any<false>(L, logits, T, E, K, renorm, ids, w, MapOut{}, stream);
     return launch_status();
   }
-  const dim3 block(256);
-  const dim3 grid(ceil_div(T, 256 / kWave));
-  const int epl = ceil_div(E, kWave);
-  if (epl <= 1)
-    route_kernel<1><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, G, TG, ids, w);
-  else if (epl <= 2)
-    route_kernel<2><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, G, TG, ids, w);
-  else if (epl <= 4)
-    route_kernel<4><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, G, TG, ids, w);
-  else if (epl <= 8)
-    route_kernel<8><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, G, TG, ids, w);
-  else
-    route_kernel<16><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, G, TG, ids, w);
+  launch_waves<false>(logits, T, E, K, renorm, G, TG, ids, w, MapOut{}, stream);
   return launch_status();
 }
 
