@@ -14,9 +14,9 @@
 //
 // Up to 256 experts (K <= 8 or the lane count, no groups) a token gets
 // L = 8, 16 or 32 lanes of a wave (at most 8 logits per lane) instead of a
-// whole wave: lane q holds experts q, q + L, ..., and each
-// round's maximum is a per-lane maximum followed by DPP steps inside the
-// group (route_lanes_kernel). Both forms give the same ids; the weights are
+// whole wave: lane q holds experts q, q + L, ..., sorted once in the lane,
+// and each round's maximum is the DPP maximum of the lanes' first keys inside
+// the group; the lane that held it moves its list up (route_lanes_kernel). Both forms give the same ids; the weights are
 // the same softmax with the sums taken in a different order, and moe_route,
 // moe_forward and the fused route + slot map of moe_forward all take the
 // same form for a given shape, so their bits agree.
@@ -56,6 +56,32 @@ struct MapOut {
   uint8_t* mask;
 };
 
+// Sorts n <= 8 keys into descending order with a comparator network
+// (Batcher's odd-even merge sort: 1, 5 or 19 compare-exchanges).
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t (&k)[N]) {
+  auto cx = [&](int a, int b) {
+    const uint64_t hi = k[a] > k[b] ? k[a] : k[b];
+    const uint64_t lo = k[a] > k[b] ? k[b] : k[a];
+    k[a] = hi;
+    k[b] = lo;
+  };
+  if constexpr (N == 2) {
+    cx(0, 1);
+  } else if constexpr (N == 4) {
+    cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
+  } else if constexpr (N == 8) {
+    cx(0, 1); cx(2, 3); cx(4, 5); cx(6, 7);
+    cx(0, 2); cx(1, 3); cx(4, 6); cx(5, 7);
+    cx(1, 2); cx(5, 6);
+    cx(0, 4); cx(1, 5); cx(2, 6); cx(3, 7);
+    cx(2, 4); cx(3, 5);
+    cx(1, 2); cx(3, 4); cx(5, 6);
+  } else {
+    static_assert(N == 1, "1, 2, 4 or 8 keys per lane");
+  }
+}
+
 // L lanes per token, EPL logits per lane (a power of two); K <= L,
 // E <= L * EPL. Lanes of
 // tokens past T carry empty keys and store nothing, but stay active, so every
@@ -84,23 +110,19 @@ __global__ __launch_bounds__(256) void route_lanes_kernel(const float* __restric
     }
   }
 
-  // K rounds; lane k of the group keeps the k-th selection's key.
+  // K rounds; lane k of the group keeps the k-th selection's key. The
+  // lane's keys are sorted once, so a round's candidate is key[0] and only
+  // the lane holding the group's maximum (keys are unique) moves its list up.
+  sort_desc<EPL>(key);
   uint64_t my_key = 0;
   uint64_t top = 0;
   for (int k = 0; k < K; ++k) {
-    // the lane's maximum as a tree (depth log2 EPL rather than EPL - 1)
-    uint64_t b[EPL];
+    const uint64_t best = group_max_u64<L>(key[0]);
+    // all ones in the lane that held it (as a bit mask: one select per word)
+    const uint64_t mv = 0ull - (uint64_t)(key[0] == best);
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) b[j] = key[j];
-#pragma unroll
-    for (int h = EPL / 2; h >= 1; h /= 2)
-#pragma unroll
-      for (int j = 0; j < h; ++j) b[j] = b[j + h] > b[j] ? b[j + h] : b[j];
-    const uint64_t best = group_max_u64<L>(b[0]);
-    const int e = (int)(0xffffffffu - (uint32_t)best);
-#pragma unroll
-    for (int j = 0; j < EPL; ++j)
-      if (q + L * j == e) key[j] = 0;
+    for (int j = 0; j + 1 < EPL; ++j) key[j] = (key[j + 1] & mv) | (key[j] & ~mv);
+    key[EPL - 1] &= ~mv;
     if (q == k) my_key = best;
     if (k == 0) top = best;
   }
