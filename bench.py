@@ -16,6 +16,12 @@ The dominant kernel (grouped GEMM 1) is timed by the events around it.
 
 --copy-probe runs only a plain device copy of a known size (for scaling the
 HBM byte counters of a profiler run) and exits.
+
+On bf16 workloads the line also carries `mfma_ceiling`: the sustained bf16
+MFMA rate of the chip measured just before (moe_expert_dispatch_amd/probe/
+mfma_ceiling, a separate process), with the MFMAs alone and with the operand
+movement of the GEMM's K-loop; the chip lowers its clock under load, so the
+2.5 PFLOP/s peak is not reached by either (--no-mfma-ceiling skips it).
 """
 from __future__ import annotations
 
@@ -49,6 +55,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--no-mfma-ceiling", action="store_true")
     ap.add_argument("--a2a", action="store_true",
                     help="time the all-to-all dispatch path on an expert-parallel workload")
     ap.add_argument("--ep-rank", type=int, default=0,
@@ -140,6 +147,27 @@ def run_a2a(args):
            "dispatch_frac_of_hbm": d_bytes / (t_d * 1e6) / PEAK_HBM_GBPS,
            "gather_sum_frac_of_hbm": g_bytes / (t_g * 1e6) / PEAK_HBM_GBPS}
     print(json.dumps(res), flush=True)
+
+
+def mfma_ceiling():
+    """Runs the MFMA ceiling program as a child process (before this process
+    touches the GPU) and returns its two rates, or a reason it could not."""
+    import subprocess
+    prog = os.path.join(ROOT, "moe_expert_dispatch_amd", "probe", "mfma_ceiling")
+    if not os.path.exists(prog):
+        return {"error": "program not built"}
+    try:
+        res = subprocess.run([prog], capture_output=True, text=True, timeout=120)
+    except subprocess.TimeoutExpired:
+        return {"error": "timed out"}
+    if res.returncode != 0:
+        return {"error": f"exit status {res.returncode}: {res.stderr.strip()[-200:]}"}
+    rates = {}
+    for line in res.stdout.splitlines():
+        rec = json.loads(line)
+        rates[rec["mode"] + "_tflops"] = rec["tflops"]
+    rates["program"] = "moe_expert_dispatch_amd/probe/mfma_ceiling"
+    return rates
 
 
 def kernel_source_digest(paths):
@@ -255,9 +283,12 @@ def main():
     if args.a2a:
         run_a2a(args)
         return
+    cfg = CONFIGS[args.workload]
+    ceiling = None
+    if cfg.dtype == "bf16" and not args.no_mfma_ceiling:
+        ceiling = mfma_ceiling()
     moe.lib()
     dev = torch.device("cuda:0")
-    cfg = CONFIGS[args.workload]
     rank = args.ep_rank
     if not 0 <= rank < cfg.ep_size:
         print(f"--ep-rank must be in [0, {cfg.ep_size}) for {cfg.name}", file=sys.stderr)
@@ -400,6 +431,9 @@ def main():
                      {"bound": "alu", "kernel": "grouped_gemm_f32 gate/up + SwiGLU (FMA)",
                       "achieved": gu_tflops, "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
                       "frac": gu_tflops / PEAK_F32_TFLOPS, "traffic": None}),
+        "mfma_ceiling": (dict(ceiling, gate_up_frac_of_operand_movement=(
+            gu_tflops / ceiling["operand_movement_tflops"]))
+            if ceiling and "operand_movement_tflops" in ceiling else ceiling),
         "grouped_gemm_tflops": gemm_tflops,
         "grouped_gemm_frac_of_bf16_peak": gemm_tflops / PEAK_BF16_TFLOPS,
         "grouped_gemm_frac_of_peak": gemm_tflops / peak_tf,

@@ -20,6 +20,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libmoe_hip.so")
+# Stand-alone measurement program (not part of the library): the chip's
+# sustained bf16 MFMA rate alone and with the GEMM's operand movement.
+PROBE_SRC = os.path.join(HERE, "probe", "mfma_ceiling.hip")
+PROBE_BIN = os.path.join(HERE, "probe", "mfma_ceiling")
 ARCH = "gfx950"
 
 
@@ -127,12 +131,15 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     cc = hipcc()
     objs = [os.path.join(BUILD_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
     jobs = jobs or min(len(srcs), os.cpu_count() or 1, 16)
+    probe_tmp = PROBE_BIN + ".tmp"
     with _fut.ThreadPoolExecutor(jobs) as ex:
         futs = [ex.submit(_run, [cc, *COMPILE_FLAGS, "-c", s, "-o", o], verbose,
                           s if os.path.basename(s) in NO_SCRATCH else None)
                 for s, o in zip(srcs, objs)]
+        futs.append(ex.submit(_run, [cc, *COMPILE_FLAGS, PROBE_SRC, "-o", probe_tmp], verbose))
         for f in futs:
             f.result()
+    os.replace(probe_tmp, PROBE_BIN)
     tmp = LIB_PATH + ".tmp"
     _run([cc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB_PATH)

@@ -77,6 +77,5 @@ __device__ __forceinline__ void gather_rows(const uint4* __restrict__ src, int n
   }
 }
 
-
 }  // namespace
 }  // namespace moe

@@ -1,0 +1,208 @@
+// Sustained bf16 MFMA rate of the chip, alone and with the operand movement of
+// the grouped GEMM's K-loop, as a ceiling to read the GEMM's rate against.
+//
+//   mfma_ceiling [iterations]      (prints one JSON line per mode)
+//
+// The 2.5 PFLOP/s bf16 figure assumes every matrix core busy at 2.4 GHz; under
+// load the chip lowers its clock to stay inside its power limit, and how far
+// depends on what else moves. All modes run the grouped GEMM's launch shape
+// (one 512-thread block per CU, 8 waves, 2 per SIMD, a 128 x 64 wave tile of
+// v_mfma_f32_32x32x16_bf16: per 16-wide K step, 2 weight fragments x 4 row
+// fragments, 8 MFMAs into 8 accumulators) on random bf16 operands (all-zero
+// ones in the first mode):
+//
+//   mfma_zero:       the MFMAs alone on all-zero operands (the same
+//                    instructions with no data toggling: the power the
+//                    operands' values cost).
+//   mfma_only:       the MFMAs alone, operands rotating through registers.
+//   operand_movement: the same MFMAs plus, at the GEMM's rates, the LDS reads
+//                    of every fragment (6 ds_read_b128 per K step, read ahead
+//                    one step) and the direct-to-LDS operand loads of a
+//                    256 x 256 tile (8 buffer_load_dwordx4 ... lds per wave per
+//                    64-wide K slice, 1 KB each, from a 2 MiB buffer that stays
+//                    in L2), issued after a workgroup barrier in the slice's
+//                    last K step, as the GEMM issues them. No epilogue, no
+//                    L2 misses, no row gather.
+//
+// Every access is in bounds by construction (indices masked to the buffers),
+// and every loop has a fixed trip count. The result is written only so that
+// the compiler keeps the work.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <type_traits>
+#include <vector>
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int kThreads = 512;
+constexpr int kFragVecs = 2048;         // 32 KB of LDS fragments (16-byte vectors)
+constexpr int kDmaVecs = 1024;          // 16 KB of LDS written by the operand loads
+constexpr uint32_t kSrcBytes = 2u << 20;  // operand-load source (L2-resident)
+constexpr int kInVecs = 96 * 64;        // random fragments in device memory
+
+template <bool MOVE, bool ZERO = false>
+__global__ __launch_bounds__(kThreads) void mfma_ceiling_kernel(const bf16x8_t* __restrict__ in,
+                                                                const uint4* __restrict__ src,
+                                                                float* __restrict__ out,
+                                                                int iters) {
+  __shared__ uint4 lds[kFragVecs + kDmaVecs];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;  // the GEMM's 2 x 4 wave layout
+  for (int v = threadIdx.x; v < kFragVecs; v += kThreads) {
+    const bf16x8_t t = in[v];
+    lds[v] = *reinterpret_cast<const uint4*>(&t);
+  }
+  __syncthreads();
+  // the two waves of a SIMD (wn equal) share weight fragments, as in the GEMM
+  bf16x8_t a[8], b[4];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a[k] = ZERO ? bf16x8_t{} : in[(wm * 8 + k) * 64 + lane];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) b[k] = ZERO ? bf16x8_t{} : in[(16 + wn * 4 + k) * 64 + lane];
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint4*>(src), (short)0, (int)kSrcBytes, 0x00020000);
+  const uint32_t frag_base = (uint32_t)(uintptr_t)(lds_ptr_t)lds + (uint32_t)lane * 16u;
+  floatx16 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = floatx16{};
+
+  for (int it = 0; it < iters; ++it) {  // one 64-wide K slice per iteration
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (MOVE) {
+        // next step's fragments: 4 row + 2 weight, 1 KB per wave each
+        const int q0 = ((it * 4 + s) * 6 + wave * 3) & 31;
+        asm volatile("ds_read_b128 %0, %1" : "=v"(a[(4 * (s + 1) + 0) & 7]) : "v"(frag_base + ((q0 + 0) & 31) * 1024u));
+        asm volatile("ds_read_b128 %0, %1" : "=v"(a[(4 * (s + 1) + 1) & 7]) : "v"(frag_base + ((q0 + 1) & 31) * 1024u));
+        asm volatile("ds_read_b128 %0, %1" : "=v"(a[(4 * (s + 1) + 2) & 7]) : "v"(frag_base + ((q0 + 2) & 31) * 1024u));
+        asm volatile("ds_read_b128 %0, %1" : "=v"(a[(4 * (s + 1) + 3) & 7]) : "v"(frag_base + ((q0 + 3) & 31) * 1024u));
+        asm volatile("ds_read_b128 %0, %1" : "=v"(b[(2 * (s + 1) + 0) & 3]) : "v"(frag_base + ((q0 + 4) & 31) * 1024u));
+        asm volatile("ds_read_b128 %0, %1" : "=v"(b[(2 * (s + 1) + 1) & 3]) : "v"(frag_base + ((q0 + 5) & 31) * 1024u));
+        if (s == 3) {
+          __builtin_amdgcn_s_barrier();
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const uint32_t voff =
+                (uint32_t)(((it * 8 + q) & 31) * 65536 + (wave * 64 + lane) * 16);  // < 2 MiB
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (lds_ptr_t)(lds + kFragVecs + (wave * 2 + (q & 1)) * 64), 16, voff, 0, 0, 0);
+          }
+          asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int j = x >> 2, i = x & 3;
+        acc[j * 4 + i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[(2 * s + j) & 3], a[(4 * s + i) & 7],
+                                                                 acc[j * 4 + i], 0, 0, 0);
+      }
+      if (MOVE) {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
+                       "+v"(a[6]), "+v"(a[7]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += acc[c][i];
+  out[blockIdx.x * kThreads + threadIdx.x] = sum;
+}
+
+#define CHECK(x)                                                                     \
+  do {                                                                               \
+    hipError_t e_ = (x);                                                             \
+    if (e_ != hipSuccess) {                                                          \
+      fprintf(stderr, "mfma_ceiling: %s at line %d\n", hipGetErrorString(e_), __LINE__); \
+      return 1;                                                                      \
+    }                                                                                \
+  } while (0)
+
+uint16_t to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <bool MOVE, bool ZERO = false>
+int run(const char* name, const bf16x8_t* in, const uint4* src, float* out, int blocks,
+        int iters) {
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  auto kernel = mfma_ceiling_kernel<MOVE, ZERO>;
+  hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kThreads), 0, 0, in, src, out,
+                     iters);
+  CHECK(hipGetLastError());
+  CHECK(hipDeviceSynchronize());
+  std::vector<float> ms(3);
+  for (float& m : ms) {
+    CHECK(hipEventRecord(e0, 0));
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kThreads), 0, 0, in, src,
+                       out, iters);
+    CHECK(hipGetLastError());
+    CHECK(hipEventRecord(e1, 0));
+    CHECK(hipEventSynchronize(e1));
+    CHECK(hipEventElapsedTime(&m, e0, e1));
+  }
+  std::sort(ms.begin(), ms.end());
+  // 8 waves x 32 MFMAs of 32 x 32 x 16 (32768 FLOP) per iteration and block
+  const double flop = (double)blocks * 8 * iters * 32 * 32768.0;
+  printf("{\"mode\": \"%s\", \"blocks\": %d, \"iterations\": %d, \"ms\": %.3f, \"tflops\": %.1f}\n",
+         name, blocks, iters, ms[1], flop / (ms[1] * 1e9));
+  fflush(stdout);
+  CHECK(hipEventDestroy(e0));
+  CHECK(hipEventDestroy(e1));
+  return 0;
+}
+
+}  // namespace
+
+int main(int argc, char** argv) {
+  const int iters = argc > 1 ? atoi(argv[1]) : 50000;
+  if (iters < 1 || iters > 10000000) {
+    fprintf(stderr, "mfma_ceiling: iterations must be in [1, 1e7]\n");
+    return 2;
+  }
+  hipDeviceProp_t prop;
+  CHECK(hipGetDeviceProperties(&prop, 0));
+  const int blocks = prop.multiProcessorCount;  // one block per CU
+  std::vector<uint16_t> h((size_t)kInVecs * 8);
+  uint64_t st = 0x9e3779b97f4a7c15ull;
+  for (auto& v : h) {  // roughly N(0, 1): sum of four uniforms
+    st = st * 6364136223846793005ull + 1442695040888963407ull;
+    float f = 0.f;
+    for (int k = 0; k < 4; ++k) f += (float)((st >> (16 * k)) & 0xffff) / 65536.0f - 0.5f;
+    v = to_bf16(f * 1.7f);
+  }
+  bf16x8_t* in;
+  uint4* src;
+  float* out;
+  CHECK(hipMalloc(&in, h.size() * 2));
+  CHECK(hipMalloc(&src, kSrcBytes));
+  CHECK(hipMalloc(&out, (size_t)blocks * kThreads * 4));
+  CHECK(hipMemcpy(in, h.data(), h.size() * 2, hipMemcpyHostToDevice));
+  for (uint32_t off = 0; off < kSrcBytes; off += (uint32_t)(h.size() * 2))
+    CHECK(hipMemcpy((char*)src + off, h.data(), std::min<size_t>(h.size() * 2, kSrcBytes - off),
+                    hipMemcpyHostToDevice));
+  if (run<false, true>("mfma_zero", in, src, out, blocks, iters)) return 1;
+  if (run<false>("mfma_only", in, src, out, blocks, iters)) return 1;
+  if (run<true>("operand_movement", in, src, out, blocks, iters)) return 1;
+  CHECK(hipFree(in));
+  CHECK(hipFree(src));
+  CHECK(hipFree(out));
+  return 0;
+}

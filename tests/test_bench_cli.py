@@ -29,3 +29,21 @@ def test_traffic_record_follows_the_gemm_source(tmp_path, monkeypatch):
     # a record taken on other source is not used
     monkeypatch.setattr(bench, "GEMM_SRC", [str(src)])
     assert bench.gemm_traffic("redundant_slots_zipf") is None
+
+
+def test_mfma_ceiling_reads_program_output(tmp_path, monkeypatch):
+    """bench.py takes the ceiling program's two JSON lines as rates, and
+    reports a reason instead when the program is missing or fails."""
+    import bench
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.mfma_ceiling() == {"error": "program not built"}
+    prog = tmp_path / "moe_expert_dispatch_amd" / "probe" / "mfma_ceiling"
+    prog.parent.mkdir(parents=True)
+    prog.write_text("#!/bin/sh\n"
+                    "echo '{\"mode\": \"mfma_only\", \"tflops\": 1800.5}'\n"
+                    "echo '{\"mode\": \"operand_movement\", \"tflops\": 1400.0}'\n")
+    prog.chmod(0o755)
+    got = bench.mfma_ceiling()
+    assert got["mfma_only_tflops"] == 1800.5 and got["operand_movement_tflops"] == 1400.0
+    prog.write_text("#!/bin/sh\necho no device >&2\nexit 1\n")
+    assert bench.mfma_ceiling()["error"].startswith("exit status 1")
