@@ -17,11 +17,14 @@ The dominant kernel (grouped GEMM 1) is timed by the events around it.
 --copy-probe runs only a plain device copy of a known size (for scaling the
 HBM byte counters of a profiler run) and exits.
 
-On bf16 workloads the line also carries `mfma_ceiling`: the sustained bf16
-MFMA rate of the chip measured just before (moe_expert_dispatch_amd/probe/
-mfma_ceiling, a separate process), with the MFMAs alone and with the operand
-movement of the GEMM's K-loop; the chip lowers its clock under load, so the
-2.5 PFLOP/s peak is not reached by either (--no-mfma-ceiling skips it).
+On bf16 workloads the line also carries `dense_reference`, one dense bf16
+GEMM of the gate/up product's FLOPs through torch.matmul, timed after the
+steps for context (--no-dense-reference skips it), and `mfma_ceiling`: the
+sustained bf16 MFMA rate of the chip measured just before (moe_expert_
+dispatch_amd/probe/mfma_ceiling, a separate process), with the MFMAs alone
+and with the operand movement of the GEMM's K-loop; the chip lowers its clock
+under load, so the 2.5 PFLOP/s peak is not reached by either
+(--no-mfma-ceiling skips it).
 """
 from __future__ import annotations
 
@@ -56,6 +59,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--no-mfma-ceiling", action="store_true")
+    ap.add_argument("--no-dense-reference", action="store_true")
     ap.add_argument("--a2a", action="store_true",
                     help="time the all-to-all dispatch path on an expert-parallel workload")
     ap.add_argument("--ep-rank", type=int, default=0,
@@ -216,6 +220,36 @@ def staged_permute_ms(moe, x, slot, mask, S, reps=10):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / reps
+
+
+def dense_reference(M, K, N, reps=10):
+    """A library rate for context: one dense bf16 GEMM [M, K] x [K, N] of the
+    gate/up product's FLOPs through torch.matmul (the BLAS library torch
+    selects, named in the result), timed with events outside the timed
+    steps. Not part of the path."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(K, N, device="cuda", dtype=torch.bfloat16, generator=g)
+    c = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    torch.cuda.empty_cache()
+    lib = str(torch.backends.cuda.preferred_blas_library()).split(".")[-1]
+    if torch.version.hip:  # torch keeps the CUDA names for the ROCm libraries
+        lib = {"Cublaslt": "hipBLASLt", "Cublas": "rocBLAS", "Ck": "composable_kernel"}.get(lib, lib)
+    return {"library": f"torch.matmul bf16 ({lib})", "shape_mkn": [M, K, N], "ms": ms,
+            "tflops": 2.0 * M * K * N / (ms * 1e9)}
 
 
 def cpu_baseline(inp, seconds, rank=0):
@@ -400,6 +434,11 @@ def main():
     # the steps: moe_forward folds the gather into the gate/up GEMM, so this is
     # where the permutation's HBM rate is measured.
     sp_ms = staged_permute_ms(moe, x, slot, mask, S)
+    dense = None
+    if cfg.dtype == "bf16" and not args.no_dense_reference:
+        # the gate/up product's FLOPs as one dense GEMM: [P_in, H] x [H, 2I]
+        dense = dense_reference(P_in, cfg.H, 2 * cfg.I)
+        dense["gate_up_vs_dense"] = gu_tflops / dense["tflops"]
     xb = x.element_size()
     sp_bytes = 2 * 5 * P + 4 * P + 4 * P_in + cfg.T * cfg.H * xb + P_in * cfg.H * xb
 
@@ -434,6 +473,7 @@ def main():
         "mfma_ceiling": (dict(ceiling, gate_up_frac_of_operand_movement=(
             gu_tflops / ceiling["operand_movement_tflops"]))
             if ceiling and "operand_movement_tflops" in ceiling else ceiling),
+        "dense_reference": dense,
         "grouped_gemm_tflops": gemm_tflops,
         "grouped_gemm_frac_of_bf16_peak": gemm_tflops / PEAK_BF16_TFLOPS,
         "grouped_gemm_frac_of_peak": gemm_tflops / peak_tf,
