@@ -19,12 +19,12 @@ HBM byte counters of a profiler run) and exits.
 
 On bf16 workloads the line also carries `dense_reference`, one dense bf16
 GEMM of the gate/up product's FLOPs through torch.matmul, timed after the
-steps for context (--no-dense-reference skips it), and `mfma_ceiling`: the
-sustained bf16 MFMA rate of the chip measured just before (moe_expert_
-dispatch_amd/probe/mfma_ceiling, a separate process), with the MFMAs alone
-and with the operand movement of the GEMM's K-loop; the chip lowers its clock
-under load, so the 2.5 PFLOP/s peak is not reached by either
-(--no-mfma-ceiling skips it).
+steps for context (--no-dense-reference skips it). On bf16 and FP8 workloads
+it carries `mfma_ceiling`: the sustained bf16 and FP8 MFMA rates of the chip
+measured just before (moe_expert_dispatch_amd/probe/mfma_ceiling, a separate
+process), with the MFMAs alone and with the operand movement of the GEMM's
+K-loop; the chip lowers its clock under load, so the peak figures are not
+reached by either (--no-mfma-ceiling skips it).
 """
 from __future__ import annotations
 
@@ -174,6 +174,15 @@ def mfma_ceiling():
     return rates
 
 
+def ceiling_with_frac(ceiling, gu_tflops, fp8):
+    """The ceiling program's rates plus the gate/up GEMM's rate as a fraction
+    of the operand-movement rate of its own precision."""
+    key = "fp8_operand_movement_tflops" if fp8 else "operand_movement_tflops"
+    if not ceiling or key not in ceiling:
+        return ceiling
+    return dict(ceiling, gate_up_frac_of_operand_movement=gu_tflops / ceiling[key])
+
+
 def kernel_source_digest(paths):
     """SHA-256 of source files with their comments and whitespace removed: it
     changes when the code does, not when a comment does."""
@@ -319,7 +328,7 @@ def main():
         return
     cfg = CONFIGS[args.workload]
     ceiling = None
-    if cfg.dtype == "bf16" and not args.no_mfma_ceiling:
+    if cfg.dtype in ("bf16", "fp8") and not args.no_mfma_ceiling:
         ceiling = mfma_ceiling()
     moe.lib()
     dev = torch.device("cuda:0")
@@ -470,9 +479,7 @@ def main():
                      {"bound": "alu", "kernel": "grouped_gemm_f32 gate/up + SwiGLU (FMA)",
                       "achieved": gu_tflops, "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
                       "frac": gu_tflops / PEAK_F32_TFLOPS, "traffic": None}),
-        "mfma_ceiling": (dict(ceiling, gate_up_frac_of_operand_movement=(
-            gu_tflops / ceiling["operand_movement_tflops"]))
-            if ceiling and "operand_movement_tflops" in ceiling else ceiling),
+        "mfma_ceiling": ceiling_with_frac(ceiling, gu_tflops, fp8),
         "dense_reference": dense,
         "grouped_gemm_tflops": gemm_tflops,
         "grouped_gemm_frac_of_bf16_peak": gemm_tflops / PEAK_BF16_TFLOPS,

@@ -23,6 +23,12 @@
 //                    in L2), issued after a workgroup barrier in the slice's
 //                    last K step, as the GEMM issues them. No epilogue, no
 //                    L2 misses, no row gather.
+//   fp8_mfma_only, fp8_operand_movement: the same two for the FP8 (E4M3)
+//                    kernels' v_mfma_scale_f32_32x32x64_f8f6f4 on random
+//                    codes: per 64-wide K block 8 MFMAs and (moving) 12
+//                    ds_read_b128, per 128-wide slice the same 8 operand loads
+//                    per wave (the same bytes as a bf16 slice, twice the
+//                    FLOPs).
 //
 // Every access is in bounds by construction (indices masked to the buffers),
 // and every loop has a fixed trip count. The result is written only so that
@@ -41,6 +47,8 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
+typedef int int32x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kThreads = 512;
@@ -122,6 +130,94 @@ __global__ __launch_bounds__(kThreads) void mfma_ceiling_kernel(const bf16x8_t* 
   out[blockIdx.x * kThreads + threadIdx.x] = sum;
 }
 
+// FP8: fragments of 32 bytes per lane (two 16-byte reads), two sets that
+// alternate per 64-wide K block; a[set][i] row fragments, b[set][j] weight
+// fragments, MFMA (j, i) into accumulator j * 4 + i.
+template <bool MOVE>
+__global__ __launch_bounds__(kThreads) void mfma_ceiling_fp8_kernel(const uint4* __restrict__ in,
+                                                                    const uint4* __restrict__ src,
+                                                                    float* __restrict__ out,
+                                                                    int iters) {
+  __shared__ uint4 lds[kFragVecs + kDmaVecs];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  for (int v = threadIdx.x; v < kFragVecs; v += kThreads) lds[v] = in[v];
+  __syncthreads();
+  auto frag = [&](int f) {  // fragment f of `in`: 2 x 64 vectors, f < 32
+    const uint4 lo = in[(2 * f) * 64 + lane], hi = in[(2 * f + 1) * 64 + lane];
+    return int32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  int32x8_t a[2][4], b[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[t][i] = frag(wm * 8 + t * 4 + i);           // < 16
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[t][j] = frag(16 + wn * 4 + t * 2 + j);      // < 32
+  }
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint4*>(src), (short)0, (int)kSrcBytes, 0x00020000);
+  const uint32_t frag_base = (uint32_t)(uintptr_t)(lds_ptr_t)lds + (uint32_t)lane * 16u;
+  auto rd32 = [&](int32x8_t& f, uint32_t a0, uint32_t a1) {
+    int32x4_t lo, hi;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(lo) : "v"(a0));
+    asm volatile("ds_read_b128 %0, %1" : "=v"(hi) : "v"(a1));
+    f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  floatx16 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = floatx16{};
+
+  for (int it = 0; it < iters; ++it) {  // one 128-wide K slice per iteration
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int cs = kb, ns = kb ^ 1;  // current and next fragment sets
+      if (MOVE) {
+        const int q0 = ((it * 2 + kb) * 12 + wave * 3) & 31;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          rd32(a[ns][i], frag_base + ((q0 + 2 * i) & 31) * 1024u,
+               frag_base + ((q0 + 2 * i + 1) & 31) * 1024u);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          rd32(b[ns][j], frag_base + ((q0 + 8 + 2 * j) & 31) * 1024u,
+               frag_base + ((q0 + 9 + 2 * j) & 31) * 1024u);
+        if (kb == 1) {
+          __builtin_amdgcn_s_barrier();
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const uint32_t voff =
+                (uint32_t)(((it * 8 + q) & 31) * 65536 + (wave * 64 + lane) * 16);  // < 2 MiB
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (lds_ptr_t)(lds + kFragVecs + (wave * 2 + (q & 1)) * 64), 16, voff, 0, 0, 0);
+          }
+          asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int j = x >> 2, i = x & 3;
+        acc[x] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[cs][j], a[cs][i], acc[x], 0, 0,
+                                                                 0, 0, 0, 0);
+      }
+      if (MOVE) {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(a[ns][0]), "+v"(a[ns][1]), "+v"(a[ns][2]), "+v"(a[ns][3]),
+                       "+v"(b[ns][0]), "+v"(b[ns][1]));
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += acc[c][i];
+  out[blockIdx.x * kThreads + threadIdx.x] = sum;
+}
+
 #define CHECK(x)                                                                     \
   do {                                                                               \
     hipError_t e_ = (x);                                                             \
@@ -137,13 +233,13 @@ uint16_t to_bf16(float f) {
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-template <bool MOVE, bool ZERO = false>
-int run(const char* name, const bf16x8_t* in, const uint4* src, float* out, int blocks,
-        int iters) {
+// flop_per_iter: FLOPs of one iteration of one block
+template <typename Kernel, typename In>
+int run(const char* name, Kernel kernel, double flop_per_iter, const In* in, const uint4* src,
+        float* out, int blocks, int iters) {
   hipEvent_t e0, e1;
   CHECK(hipEventCreate(&e0));
   CHECK(hipEventCreate(&e1));
-  auto kernel = mfma_ceiling_kernel<MOVE, ZERO>;
   hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kThreads), 0, 0, in, src, out,
                      iters);
   CHECK(hipGetLastError());
@@ -159,8 +255,7 @@ int run(const char* name, const bf16x8_t* in, const uint4* src, float* out, int 
     CHECK(hipEventElapsedTime(&m, e0, e1));
   }
   std::sort(ms.begin(), ms.end());
-  // 8 waves x 32 MFMAs of 32 x 32 x 16 (32768 FLOP) per iteration and block
-  const double flop = (double)blocks * 8 * iters * 32 * 32768.0;
+  const double flop = (double)blocks * iters * flop_per_iter;
   printf("{\"mode\": \"%s\", \"blocks\": %d, \"iterations\": %d, \"ms\": %.3f, \"tflops\": %.1f}\n",
          name, blocks, iters, ms[1], flop / (ms[1] * 1e9));
   fflush(stdout);
@@ -198,9 +293,31 @@ int main(int argc, char** argv) {
   for (uint32_t off = 0; off < kSrcBytes; off += (uint32_t)(h.size() * 2))
     CHECK(hipMemcpy((char*)src + off, h.data(), std::min<size_t>(h.size() * 2, kSrcBytes - off),
                     hipMemcpyHostToDevice));
-  if (run<false, true>("mfma_zero", in, src, out, blocks, iters)) return 1;
-  if (run<false>("mfma_only", in, src, out, blocks, iters)) return 1;
-  if (run<true>("operand_movement", in, src, out, blocks, iters)) return 1;
+  // bf16: 8 waves x 32 MFMAs of 32 x 32 x 16 (32768 FLOP) per iteration;
+  // FP8: 8 waves x 16 MFMAs of 32 x 32 x 64 (131072 FLOP)
+  const double bf16_flop = 8.0 * 32 * 32768.0, fp8_flop = 8.0 * 16 * 131072.0;
+  if (run("mfma_zero", mfma_ceiling_kernel<false, true>, bf16_flop, in, src, out, blocks, iters))
+    return 1;
+  if (run("mfma_only", mfma_ceiling_kernel<false>, bf16_flop, in, src, out, blocks, iters))
+    return 1;
+  if (run("operand_movement", mfma_ceiling_kernel<true>, bf16_flop, in, src, out, blocks, iters))
+    return 1;
+  // random E4M3 codes, the two NaN patterns (0x7f, 0xff) avoided
+  std::vector<uint8_t> q((size_t)kInVecs * 16);
+  for (auto& v : q) {
+    st = st * 6364136223846793005ull + 1442695040888963407ull;
+    v = (uint8_t)(st >> 56);
+    if ((v & 0x7f) == 0x7f) v ^= 1;
+  }
+  uint4* in8;
+  CHECK(hipMalloc(&in8, q.size()));
+  CHECK(hipMemcpy(in8, q.data(), q.size(), hipMemcpyHostToDevice));
+  if (run("fp8_mfma_only", mfma_ceiling_fp8_kernel<false>, fp8_flop, in8, src, out, blocks, iters))
+    return 1;
+  if (run("fp8_operand_movement", mfma_ceiling_fp8_kernel<true>, fp8_flop, in8, src, out, blocks,
+          iters))
+    return 1;
+  CHECK(hipFree(in8));
   CHECK(hipFree(in));
   CHECK(hipFree(src));
   CHECK(hipFree(out));

@@ -47,3 +47,12 @@ def test_mfma_ceiling_reads_program_output(tmp_path, monkeypatch):
     assert got["mfma_only_tflops"] == 1800.5 and got["operand_movement_tflops"] == 1400.0
     prog.write_text("#!/bin/sh\necho no device >&2\nexit 1\n")
     assert bench.mfma_ceiling()["error"].startswith("exit status 1")
+
+
+def test_ceiling_fraction_uses_the_gemm_precision():
+    import bench
+    c = {"operand_movement_tflops": 1400.0, "fp8_operand_movement_tflops": 2800.0}
+    assert bench.ceiling_with_frac(c, 700.0, False)["gate_up_frac_of_operand_movement"] == 0.5
+    assert bench.ceiling_with_frac(c, 700.0, True)["gate_up_frac_of_operand_movement"] == 0.25
+    assert bench.ceiling_with_frac({"error": "x"}, 700.0, True) == {"error": "x"}
+    assert bench.ceiling_with_frac(None, 700.0, False) is None

@@ -42,5 +42,7 @@ def test_bench_line_contract():
     assert "error" not in ceil, ceil
     for mode in ("mfma_zero", "mfma_only", "operand_movement"):
         assert 0 < ceil[mode + "_tflops"] <= 2600, ceil
+    for mode in ("fp8_mfma_only", "fp8_operand_movement"):
+        assert 0 < ceil[mode + "_tflops"] <= 5200, ceil
     dense = d["dense_reference"]
     assert dense["shape_mkn"][1:] == [2048, 2 * 1408] and dense["tflops"] > 0
