@@ -86,6 +86,28 @@ def test_route_parity(dev, name):
     assert_close(np64(w), ref_w, (1e-5, 1e-9), "route weights")
 
 
+@pytest.mark.parametrize("E", [8, 64, 160, 256, 300])
+def test_route_renormalized_weights_exact(dev, E):
+    """Renormalisation divides each selected probability by their f32 sum:
+    with K = 1 that is p / p, exactly 1.0 under IEEE division; with K = 8
+    the weights sum to 1 within the rounding of the K quotients and of the
+    sum (at most 2K units of 2^-24). E = 300 takes the wave-per-token
+    router, the others the lane-group router."""
+    g = torch.Generator().manual_seed(E)
+    logits = (torch.randn(257, E, generator=g) * 3).float()
+    announce(f"route renormalised weights E={E}")
+    ids, w = moe.route(logits.to(dev), 1, True)
+    torch.cuda.synchronize()
+    assert (w.cpu() == 1.0).all()
+    ref_ids, _ = oracle.route(logits, 1, True)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    if E >= 8:
+        ids8, w8 = moe.route(logits.to(dev), 8, True)
+        torch.cuda.synchronize()
+        tot = w8.cpu().double().sum(dim=1).numpy()
+        assert np.abs(tot - 1.0).max() <= 2 * 8 * 2.0 ** -24
+
+
 # ------------------------------------------------------------------ slot map
 def _slot_map_check(dev, ids, w, E, ep_size, ep_rank, ro=None, rs=None):
     d = lambda t: None if t is None else t.to(dev)
